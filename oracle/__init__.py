@@ -1,0 +1,64 @@
+"""CPU oracle for the CalibAtt layer hot path. TEST INFRASTRUCTURE ONLY.
+
+Only the tests, the smoke check (``__graft_entry__.smoke``) and the CPU-baseline
+leg of ``bench.py`` may import or run anything in this package. The product
+path (the HIP library ``libcalibatt.so`` and its Python binding) never imports,
+calls or links it, and the two share no code: no helpers, no constants, no
+pre- or post-processing. Both consume the same seeded inputs from the
+``workloads`` module, which holds none of the method's arithmetic.
+
+What is computed, and where it is stated
+----------------------------------------
+Citations name the web page and the section on it:
+
+* [Notes] papernotes.org notes on "Accelerating Text-to-Video Generation with
+  Calibrated Sparse Attention" (ECCV 2026 notes).
+* [Abstract] the arXiv abstract of the same paper (2603.05503), as shown on
+  the mlsanity.com paper index page.
+
+``skiplist.compile_skiplist``
+    Each calibrated binary block mask becomes, for every query block, the list
+    of key blocks to compute ([Notes] Key Design 4, "Precompiled dual-path
+    execution"; Highlights). The lists are indexed by timestep, layer and head
+    ([Notes] Overall Architecture). Encoding read here: CSR, ascending key
+    blocks, plus a per-record heaviest-first order of query blocks.
+
+``attention.block_sparse_head``
+    Retained connections are computed from the current input's Q, K and V and
+    unselected ones are skipped ([Notes] Overall Architecture; [Abstract]).
+    That is exactly softmax attention restricted to the kept key blocks of each
+    query block, written out in fp64 from its definition.
+
+``attention.anchor_head``
+    Repetitive heads compute attention only for a few anchor spatial rows per
+    frame, against all keys and values, and broadcast each anchor's output to
+    its nearest spatial rows in the same frame ([Notes] Key Design 3, "Spatial
+    repetition detection"; Key Design 4; A Worked Example).
+
+``attention.layer_forward``
+    The record for (timestep, layer, head) selects the path per head: the
+    repetition flag chooses anchor rows, otherwise the block-sparse path; the
+    two paths are alternatives ([Notes] Key Design 4).
+
+Pins
+----
+Every function above is pinned by ``tests/test_oracle_*.py`` against results
+fixed by the pages or by mathematics, independent of this code: brute-force
+enumeration of skip lists, hand-derived fixtures under ``tests/golden/``,
+PyTorch's scaled-dot-product attention (fp64, CPU) with an explicit token mask,
+scipy's logsumexp, closed forms (Q = 0, constant V), exact zeros outside kept
+blocks, row sums of one, and the identical-rows property of the anchor rule.
+There are no printed attention values on the pages, so beyond these pins the
+attention outputs have no external worked example; no function here is
+"parity unpinned".
+
+Readings of points the pages leave open are listed in the module docstrings
+where they are applied (empty rows, partial last block, anchor ties, token
+order, broadcast unit).
+"""
+from .skiplist import compile_skiplist, skiplist_to_dense
+from .attention import (block_sparse_head, anchor_head, nearest_anchor_rows,
+                        layer_forward, block_tokens)
+
+__all__ = ["compile_skiplist", "skiplist_to_dense", "block_sparse_head", "anchor_head",
+           "nearest_anchor_rows", "layer_forward", "block_tokens"]
