@@ -1,0 +1,208 @@
+"""ctypes binding of libcalibatt.so (the C ABI in include/calibatt.h).
+
+Argument marshalling only: every step of the hot path runs in the library's
+HIP kernels. torch supplies device buffers (``tensor.data_ptr()``) and the
+stream handle; nothing here computes attention or skip lists. There is no
+fallback: if the library is missing, importing this module raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libcalibatt.so")
+
+OK, ERR_INVALID_ARG, ERR_CAPACITY, ERR_HIP, ERR_UNSUPPORTED = 0, 1, 2, 3, 4
+BF16, F32 = 0, 1
+MAX_HEADS, MAX_ANCHORS, MAX_NB = 256, 64, 8192
+
+EXPORTED = (
+    "calibatt_compile_skiplist", "calibatt_block_sparse_attn", "calibatt_anchor_attn",
+    "calibatt_layer_dispatch", "calibatt_last_error", "calibatt_set_kernel_events", "calibatt_version",
+)
+
+
+class CalibattError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"calibatt status {status}: {message}")
+        self.status = status
+
+
+class SkipListView(ctypes.Structure):
+    """Mirror of calibatt_skiplist_t."""
+    _fields_ = [("T", ctypes.c_int32), ("L", ctypes.c_int32), ("H", ctypes.c_int32),
+                ("N", ctypes.c_int32), ("B", ctypes.c_int32), ("nb", ctypes.c_int32),
+                ("row_ptr", ctypes.c_void_p), ("col_idx", ctypes.c_void_p), ("order", ctypes.c_void_p)]
+
+
+def _load():
+    # torch ships its own HIP runtime (same soname as /opt/rocm's). Loading it
+    # first makes the library bind to that runtime, so device pointers and
+    # streams coming from torch are valid in the library's HIP calls.
+    import torch  # noqa: F401
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is not built; run __graft_entry__.build() "
+                          "or python -m calibrated_block_sparse_skiplist_amd.build")
+    lib = ctypes.CDLL(LIB_PATH)
+    vp, i32, i64, f32 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float
+    lib.calibatt_compile_skiplist.argtypes = [vp, i32, i32, i32, i32, i32, vp, vp, i64, vp,
+                                              ctypes.POINTER(i64), vp]
+    lib.calibatt_compile_skiplist.restype = i32
+    lib.calibatt_block_sparse_attn.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, f32,
+                                               ctypes.POINTER(SkipListView), i32, i32, vp, i32, vp]
+    lib.calibatt_block_sparse_attn.restype = i32
+    lib.calibatt_anchor_attn.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, f32,
+                                         i32, i32, i32, vp, i32, vp, i32, vp]
+    lib.calibatt_anchor_attn.restype = i32
+    lib.calibatt_layer_dispatch.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, f32,
+                                            ctypes.POINTER(SkipListView), i32, i32, vp,
+                                            i32, i32, i32, vp, i32, vp]
+    lib.calibatt_layer_dispatch.restype = i32
+    lib.calibatt_last_error.argtypes = []
+    lib.calibatt_last_error.restype = ctypes.c_char_p
+    lib.calibatt_set_kernel_events.argtypes = [vp, vp]
+    lib.calibatt_set_kernel_events.restype = None
+    lib.calibatt_version.argtypes = []
+    lib.calibatt_version.restype = i32
+    return lib
+
+
+lib = _load()
+
+
+def last_error() -> str:
+    return lib.calibatt_last_error().decode()
+
+
+def _check(status: int) -> None:
+    if status != OK:
+        raise CalibattError(status, last_error())
+
+
+def _ptr(t) -> int | None:
+    """Device address of a torch tensor (None for None)."""
+    if t is None:
+        return None
+    if not t.is_contiguous():
+        raise ValueError("tensors must be contiguous")
+    return t.data_ptr()
+
+
+def _stream(stream) -> int | None:
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    return getattr(stream, "cuda_stream", stream)
+
+
+def _host_i32(values):
+    if values is None:
+        return None, 0
+    arr = np.ascontiguousarray(np.asarray(values, dtype=np.int32))
+    return arr, len(arr)
+
+
+def _dtype_code(t) -> int:
+    import torch
+    if t.dtype == torch.bfloat16:
+        return BF16
+    if t.dtype == torch.float32:
+        return F32
+    raise ValueError(f"unsupported dtype {t.dtype}")
+
+
+@dataclass
+class SkipList:
+    """A compiled dictionary held in device tensors (row_ptr, col_idx, order)."""
+    T: int
+    L: int
+    H: int
+    N: int
+    B: int
+    nb: int
+    row_ptr: object
+    col_idx: object
+    order: object
+    nnz: int
+
+    def view(self) -> SkipListView:
+        return SkipListView(self.T, self.L, self.H, self.N, self.B, self.nb,
+                            _ptr(self.row_ptr), _ptr(self.col_idx),
+                            _ptr(self.order) if self.order is not None else None)
+
+
+def calibatt_compile_skiplist(masks, T, L, H, N, B, row_ptr, col_idx, col_capacity, order, stream=None) -> int:
+    """Raw call: device tensors in, returns nnz (raises on error, CAPACITY included)."""
+    nnz = ctypes.c_int64(-1)
+    st = lib.calibatt_compile_skiplist(_ptr(masks), T, L, H, N, B, _ptr(row_ptr), _ptr(col_idx),
+                                       int(col_capacity), _ptr(order), ctypes.byref(nnz), _stream(stream))
+    if st == ERR_CAPACITY:
+        raise CalibattError(st, last_error() + f" (nnz={nnz.value})")
+    _check(st)
+    return nnz.value
+
+
+def compile_skiplist(masks, N: int, B: int, with_order: bool = True, stream=None) -> SkipList:
+    """Compile uint8 device masks [T, L, H, nb, nb] into a SkipList (allocates with torch)."""
+    import torch
+    T, L, H, nb, nb2 = masks.shape
+    if nb != nb2 or nb != -(-N // B):
+        raise ValueError("masks must be [T, L, H, nb, nb] with nb = ceil(N/B)")
+    dev = masks.device
+    rows = T * L * H * nb
+    row_ptr = torch.empty(rows + 1, dtype=torch.int64, device=dev)
+    nnz = calibatt_compile_skiplist(masks, T, L, H, N, B, row_ptr, None, 0, None, stream)
+    col_idx = torch.empty(max(nnz, 1), dtype=torch.int32, device=dev)
+    order = torch.empty(rows, dtype=torch.int32, device=dev) if with_order else None
+    calibatt_compile_skiplist(masks, T, L, H, N, B, row_ptr, col_idx, col_idx.numel(), order, stream)
+    return SkipList(T, L, H, N, B, nb, row_ptr, col_idx, order, nnz)
+
+
+def calibatt_block_sparse_attn(q, k, v, o, lse, sl: SkipList, t: int, l: int, heads=None,
+                               scale: float | None = None, stream=None) -> None:
+    H, N, d = q.shape
+    scale = float(np.float32(1.0 / np.sqrt(d))) if scale is None else scale
+    harr, nh = _host_i32(heads)
+    view = sl.view()
+    _check(lib.calibatt_block_sparse_attn(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), H, N, d,
+                                          _dtype_code(q), scale, ctypes.byref(view), t, l,
+                                          harr.ctypes.data if harr is not None else None, nh,
+                                          _stream(stream)))
+
+
+def calibatt_anchor_attn(q, k, v, o, lse, F: int, R: int, C: int, anchor_rows, heads=None,
+                         scale: float | None = None, stream=None) -> None:
+    H, N, d = q.shape
+    scale = float(np.float32(1.0 / np.sqrt(d))) if scale is None else scale
+    aarr, ka = _host_i32(anchor_rows)
+    harr, nh = _host_i32(heads)
+    _check(lib.calibatt_anchor_attn(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), H, N, d,
+                                    _dtype_code(q), scale, F, R, C, aarr.ctypes.data, ka,
+                                    harr.ctypes.data if harr is not None else None, nh, _stream(stream)))
+
+
+def calibatt_layer_dispatch(q, k, v, o, lse, sl: SkipList, t: int, l: int, rep_flags, F: int, R: int,
+                            C: int, anchor_rows, scale: float | None = None, stream=None) -> None:
+    H, N, d = q.shape
+    scale = float(np.float32(1.0 / np.sqrt(d))) if scale is None else scale
+    flags = np.ascontiguousarray(np.asarray(rep_flags, dtype=np.uint8))
+    if flags.shape != (sl.T, sl.L, sl.H):
+        raise ValueError("rep_flags must be [T, L, H] of the dictionary")
+    aarr, ka = _host_i32(anchor_rows)
+    view = sl.view()
+    _check(lib.calibatt_layer_dispatch(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), H, N, d,
+                                       _dtype_code(q), scale, ctypes.byref(view), t, l,
+                                       flags.ctypes.data, F, R, C, aarr.ctypes.data, ka, _stream(stream)))
+
+
+def calibatt_set_kernel_events(begin, end) -> None:
+    """begin/end: raw hipEvent_t handles (ints) or None."""
+    lib.calibatt_set_kernel_events(begin, end)
+
+
+def calibatt_version() -> int:
+    return lib.calibatt_version()

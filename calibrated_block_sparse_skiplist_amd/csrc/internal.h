@@ -1,0 +1,77 @@
+// Internal declarations shared by the host entry points and the kernels of
+// libcalibatt.so. Nothing here is part of the C ABI (see include/calibatt.h).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "calibatt.h"
+
+namespace calibatt {
+
+// One attention launch: a list of work items, each a tile of up to `blk`
+// queries of one head together with the key blocks it visits.
+//   * anchor items come first: head anchor_heads[i / anchor_tiles], tile
+//     i % anchor_tiles of the gathered anchor queries (F*k*C of them, in
+//     (frame, anchor, column) order), visiting every key block;
+//   * block-sparse items follow: head sparse_heads[j / nb] visits the list of
+//     query block order[rec*nb + j % nb] (or j % nb when order is NULL).
+// The grid is therefore heaviest-first: anchor tiles see all nb key blocks,
+// and each head's query blocks come in descending kept count.
+struct AttnParams {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* o;
+  float* lse;
+  int64_t head_stride;      // N * d elements
+  int32_t N;
+  int32_t nb;               // key (and query) blocks of `blk` tokens
+  float scale;              // softmax scale
+  float scale_log2;         // scale * log2(e)
+  // block-sparse items
+  const int64_t* row_ptr;
+  const int32_t* col_idx;
+  const int32_t* order;
+  int64_t rec_row0;         // skip-list row of (t, l, head 0, block 0)
+  int32_t rec_head_rows;    // rows per record (= nb)
+  int32_t n_sparse;
+  // anchor items
+  int32_t n_anchor;
+  int32_t anchor_tiles;
+  int32_t n_anchor_q;       // F * k * C
+  int32_t F, R, C, ka;       // frames, rows, columns, anchor rows per frame
+  int32_t anchors[CALIBATT_MAX_ANCHORS];
+  int32_t sparse_heads[CALIBATT_MAX_HEADS];
+  int32_t anchor_heads[CALIBATT_MAX_HEADS];
+};
+
+// Copy of anchor-row outputs to the other spatial rows of each frame.
+struct BcastParams {
+  void* o;
+  float* lse;
+  int64_t head_stride;      // N * d elements
+  int32_t N, d, esize;      // esize: bytes per element of o
+  int32_t F, R, C, ka;       // frames, rows, columns, anchor rows per frame
+  int32_t n_heads;
+  int32_t anchors[CALIBATT_MAX_ANCHORS];
+  int32_t heads[CALIBATT_MAX_HEADS];
+};
+
+inline int64_t attn_items(const AttnParams& p) {
+  return (int64_t)p.n_anchor * p.anchor_tiles + (int64_t)p.n_sparse * p.nb;
+}
+
+// Launchers (each returns the status of the launch itself).
+hipError_t launch_attn_bf16(const AttnParams& p, int d, int blk, hipStream_t s);
+hipError_t launch_attn_f32(const AttnParams& p, int d, int blk, hipStream_t s);
+hipError_t launch_broadcast(const BcastParams& p, hipStream_t s);
+
+hipError_t launch_compile_count_scan(const uint8_t* masks, int64_t rows, int nb, int64_t* row_ptr,
+                                     hipStream_t s);
+hipError_t launch_compile_fill(const uint8_t* masks, int64_t rows, int nb, const int64_t* row_ptr,
+                               int32_t* col_idx, hipStream_t s);
+hipError_t launch_compile_order(const int64_t* row_ptr, int64_t records, int nb, int32_t* order,
+                                hipStream_t s);
+
+}  // namespace calibatt

@@ -1,0 +1,181 @@
+/*
+ * calibatt.h -- C ABI of libcalibatt.so, the MI355X (gfx950) inference hot path
+ * of calibrated block-sparse attention (CalibAtt) for one transformer layer.
+ *
+ * What the method computes (web pages this library follows):
+ *  [Notes]    papernotes.org notes on "Accelerating Text-to-Video Generation with
+ *             Calibrated Sparse Attention" (ECCV 2026 notes).
+ *  [Abstract] the paper's arXiv abstract (2603.05503) on its mlsanity.com page.
+ *
+ * Offline calibration produces, per (timestep, layer, head), a binary mask over
+ * 128x128 FlashAttention blocks and a spatial-repetition flag ([Notes] Overall
+ * Architecture). Each mask becomes a read-only skip list, per query block, of
+ * the key blocks to compute, resident on the GPU ([Notes] Key Design 4). At
+ * inference the record selected by (t, l, h) drives one of two alternative
+ * paths per head: block-sparse attention over the listed blocks for
+ * non-repetitive heads, or anchor-row attention plus broadcast to the
+ * neighbouring spatial rows for repetitive heads ([Notes] Key Designs 3 and 4).
+ *
+ * Conventions shared by every entry point
+ *  - All array pointers are device pointers (hipMalloc / torch CUDA tensors)
+ *    unless marked "host". The caller owns every buffer; the library never
+ *    frees caller memory and keeps no state between calls.
+ *  - Tensors Q, K, V, O are [H][N][d], contiguous, row-major. Token order is
+ *    n = (f*R + r)*C + c: frame f, spatial row r, column c.
+ *  - Blocks: query/key block b covers tokens [b*B, min((b+1)*B, N));
+ *    nb = ceil(N / B). A partial last block has fewer tokens, nothing is padded.
+ *  - lse (optional, may be NULL) is float32 [H][N], natural-log units:
+ *    lse_i = log sum_j exp(scale * q_i . k_j) over the keys row i attends to.
+ *  - Supported: d in {64, 128}; B in {64, 128}; dtype bf16 (the performance
+ *    path, fp32 accumulation and softmax) or fp32 (a correctness path with
+ *    fp32 arithmetic throughout). scale must be finite and > 0.
+ *  - `stream` is a hipStream_t passed as void* (NULL = the null stream). The
+ *    attention calls are asynchronous: they only enqueue kernels on `stream`.
+ *  - Errors: arguments are checked on the host before anything is enqueued.
+ *    A bad argument returns CALIBATT_ERR_INVALID_ARG and touches no output; a
+ *    failed HIP call returns CALIBATT_ERR_HIP. calibatt_last_error() then
+ *    describes the failure. Faults inside kernels surface at the caller's next
+ *    synchronisation of `stream`. The library is reentrant across threads;
+ *    the error message is thread-local.
+ */
+#ifndef CALIBATT_H
+#define CALIBATT_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  CALIBATT_OK = 0,
+  CALIBATT_ERR_INVALID_ARG = 1,
+  CALIBATT_ERR_CAPACITY = 2,
+  CALIBATT_ERR_HIP = 3,
+  CALIBATT_ERR_UNSUPPORTED = 4
+} calibatt_status_t;
+
+typedef enum { CALIBATT_BF16 = 0, CALIBATT_F32 = 1 } calibatt_dtype_t;
+
+/* Limits of one call. */
+#define CALIBATT_MAX_HEADS 256    /* heads taking part in one attention call */
+#define CALIBATT_MAX_ANCHORS 64   /* anchor rows per frame */
+#define CALIBATT_MAX_NB 8192      /* blocks per sequence */
+
+/*
+ * A compiled skip-list dictionary (a POD view of caller-owned device arrays,
+ * as produced by calibatt_compile_skiplist).
+ *   T, L, H : timesteps, layers and heads the dictionary covers
+ *   N, B, nb: tokens, block size, blocks per sequence (nb = ceil(N/B))
+ *   row_ptr : int64 [T*L*H*nb + 1]; record (t, l, h) has id (t*L + l)*H + h
+ *             and its query block r is row id*nb + r.
+ *   col_idx : int32 [row_ptr[T*L*H*nb]], each row's key blocks, ascending.
+ *   order   : int32 [T*L*H*nb] or NULL; per record, query blocks by
+ *             descending kept count (ties by index). Used only to order work.
+ */
+typedef struct {
+  int32_t T, L, H, N, B, nb;
+  const int64_t* row_ptr;
+  const int32_t* col_idx;
+  const int32_t* order;
+} calibatt_skiplist_t;
+
+/*
+ * Compile binary block masks into skip lists ([Notes] Key Design 4: each mask
+ * becomes, per query block, the read-only list of key blocks to compute, kept
+ * on the GPU; Overall Architecture: indexed by timestep, layer and head).
+ *
+ *   masks     uint8 [T][L][H][nb][nb], device; entry [t][l][h][r][c] != 0
+ *             means "compute query block r against key block c".
+ *   T, L, H   >= 1; N >= 1 tokens; B >= 1 block size; nb = ceil(N/B) <= CALIBATT_MAX_NB.
+ *   row_ptr   int64 [T*L*H*nb + 1], device, written (row_ptr[0] = 0).
+ *   col_idx   int32 [col_capacity], device, written; may be NULL to query the
+ *             size only (then only row_ptr and *nnz_out are written).
+ *   order     int32 [T*L*H*nb], device, written; may be NULL.
+ *   nnz_out   host; receives the number of kept blocks (always, when OK or CAPACITY).
+ * Returns CALIBATT_ERR_CAPACITY when col_capacity < nnz (col_idx and order are
+ * then not written). This is the only call that synchronises `stream` (to
+ * read nnz back); it runs offline, before generation.
+ */
+calibatt_status_t calibatt_compile_skiplist(const uint8_t* masks, int32_t T, int32_t L, int32_t H,
+                                            int32_t N, int32_t B, int64_t* row_ptr, int32_t* col_idx,
+                                            int64_t col_capacity, int32_t* order, int64_t* nnz_out,
+                                            void* stream);
+
+/*
+ * Block-sparse attention for selected heads of one layer-call ([Notes]
+ * Overall Architecture and Key Design 4; [Abstract]: retained connections are
+ * computed densely from the current Q, K, V, unselected ones are skipped).
+ * For every listed head h and query block r of record (t, l, h):
+ *   O[h][I_r] = softmax(scale * Q[h][I_r] K[h][J]^T) V[h][J],
+ * J = union of the key blocks in row r's list. An empty list gives O = 0 and
+ * lse = -inf. Only rows of the listed heads are written.
+ *   q, k, v   [H][N][d] (bf16 or fp32 per dtype), device, read-only.
+ *   o         [H][N][d], device, written for the listed heads.
+ *   lse       float [H][N], device, or NULL.
+ *   sl        host pointer to a skip-list view with sl->H == H, sl->N == N,
+ *             sl->B in {64, 128}, 0 <= t < sl->T, 0 <= l < sl->L.
+ *   heads     host int32 [n_heads], distinct head indices in [0, H), or NULL
+ *             for all H heads (then n_heads is ignored).
+ */
+calibatt_status_t calibatt_block_sparse_attn(const void* q, const void* k, const void* v, void* o,
+                                             float* lse, int32_t H, int32_t N, int32_t d,
+                                             calibatt_dtype_t dtype, float scale,
+                                             const calibatt_skiplist_t* sl, int32_t t, int32_t l,
+                                             const int32_t* heads, int32_t n_heads, void* stream);
+
+/*
+ * Anchor-row attention with broadcast for selected (repetitive) heads
+ * ([Notes] Key Design 3: only anchor rows compute attention, against all keys
+ * and values; each anchor's output is broadcast to its nearest spatial rows
+ * within the frame; k anchors reduce a frame's queries from R*C to k*C).
+ *   N must equal F*R*C. anchor_rows: host int32 [k], strictly ascending, in
+ *   [0, R); 1 <= k <= min(R, CALIBATT_MAX_ANCHORS). Each row r copies the
+ *   anchor a minimising |r - a| (ties to the smaller a), column by column, in
+ *   the same frame; lse is copied the same way. Tiling is internal (128
+ *   queries and keys per tile for bf16, 64 for fp32); the result does not
+ *   depend on it.
+ *   heads: host int32 [n_heads] or NULL for all heads.
+ */
+calibatt_status_t calibatt_anchor_attn(const void* q, const void* k, const void* v, void* o,
+                                       float* lse, int32_t H, int32_t N, int32_t d,
+                                       calibatt_dtype_t dtype, float scale,
+                                       int32_t F, int32_t R, int32_t C, const int32_t* anchor_rows,
+                                       int32_t k_anchors, const int32_t* heads, int32_t n_heads,
+                                       void* stream);
+
+/*
+ * One attention layer-call with per-head dual-path dispatch ([Notes] Key
+ * Design 4: the current timestep, layer and head select the record; the
+ * repetition flag chooses anchor-row attention, otherwise block-sparse
+ * attention; the paths are alternatives). rep_flags is host uint8 [T][L][H]
+ * with T, L, H taken from *sl. Every head of O (and lse) is written. All work
+ * is enqueued on `stream` without synchronising.
+ */
+calibatt_status_t calibatt_layer_dispatch(const void* q, const void* k, const void* v, void* o,
+                                          float* lse, int32_t H, int32_t N, int32_t d,
+                                          calibatt_dtype_t dtype, float scale,
+                                          const calibatt_skiplist_t* sl, int32_t t, int32_t l,
+                                          const uint8_t* rep_flags, int32_t F, int32_t R, int32_t C,
+                                          const int32_t* anchor_rows, int32_t k_anchors, void* stream);
+
+/* Message for the last non-OK status returned on this thread ("" if none). */
+const char* calibatt_last_error(void);
+
+/*
+ * Timing hook for benchmarks: the next attention launch made on this thread
+ * by calibatt_block_sparse_attn, calibatt_anchor_attn or
+ * calibatt_layer_dispatch records hipEvent_t `begin` right before the
+ * attention kernel and `end` right after it, on the same stream; the hook
+ * then clears itself. Pass NULL, NULL to clear it explicitly.
+ */
+void calibatt_set_kernel_events(void* begin, void* end);
+
+/* Library version as major*10000 + minor*100 + patch. */
+int32_t calibatt_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* CALIBATT_H */

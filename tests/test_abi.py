@@ -1,0 +1,130 @@
+"""The C-ABI library loads, exports what include/calibatt.h declares, and rejects
+bad arguments on the host before anything is enqueued (CPU only).
+
+Every call below is invalid by construction, so it returns before any HIP
+call: device pointers are placeholders that are never dereferenced.
+"""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "calibatt.h")
+
+cal = pytest.importorskip("calibrated_block_sparse_skiplist_amd._lib")
+lib = cal.lib
+INVALID = cal.ERR_INVALID_ARG
+P = 0x1000   # placeholder device address; never dereferenced by a rejected call
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(calibatt_[a-z_]+)\s*\(", text)))
+
+
+def test_every_declared_symbol_is_exported():
+    names = declared_functions()
+    assert set(names) == set(cal.EXPORTED)
+    for n in names:
+        assert hasattr(lib, n), n
+        assert ctypes.cast(getattr(lib, n), ctypes.c_void_p).value
+
+
+def test_version_and_error_string():
+    assert lib.calibatt_version() == 100
+    assert isinstance(lib.calibatt_last_error(), bytes)
+
+
+def _view(T=1, L=1, H=2, N=1000, B=128, nb=8):
+    return cal.SkipListView(T, L, H, N, B, nb, P, P, None)
+
+
+def _sparse(**kw):
+    a = dict(q=P, k=P, v=P, o=P, lse=None, H=2, N=1000, d=128, dtype=cal.BF16, scale=0.088,
+             view=_view(), t=0, l=0, heads=None, nh=0)
+    a.update(kw)
+    return lib.calibatt_block_sparse_attn(a["q"], a["k"], a["v"], a["o"], a["lse"], a["H"], a["N"], a["d"],
+                                          a["dtype"], a["scale"], ctypes.byref(a["view"]) if a["view"] else None,
+                                          a["t"], a["l"], a["heads"], a["nh"], None)
+
+
+@pytest.mark.parametrize("kw,msg", [
+    (dict(q=None), "non-NULL"),
+    (dict(d=96), "d = 96"),
+    (dict(dtype=7), "dtype"),
+    (dict(scale=0.0), "scale"),
+    (dict(scale=float("nan")), "scale"),
+    (dict(H=3), "skip list is for"),
+    (dict(view=None), "NULL"),
+    (dict(view=_view(B=32, nb=32)), "block size"),
+    (dict(view=_view(nb=9)), "nb"),
+    (dict(t=1), "outside the dictionary"),
+    (dict(l=-1), "outside the dictionary"),
+])
+def test_block_sparse_rejects(kw, msg):
+    assert _sparse(**kw) == INVALID
+    assert msg in cal.last_error()
+
+
+def test_block_sparse_rejects_bad_heads():
+    bad = np.array([0, 2], dtype=np.int32)
+    assert _sparse(heads=bad.ctypes.data, nh=2) == INVALID
+    assert "out of range" in cal.last_error()
+    dup = np.array([1, 1], dtype=np.int32)
+    assert _sparse(heads=dup.ctypes.data, nh=2) == INVALID
+    assert "twice" in cal.last_error()
+
+
+def _anchor(N=600, F=3, R=10, C=20, anchors=(2, 7), d=64, dtype=cal.BF16):
+    arr = np.array(anchors, dtype=np.int32)
+    return lib.calibatt_anchor_attn(P, P, P, P, None, 1, N, d, dtype, 0.125, F, R, C,
+                                    arr.ctypes.data if len(arr) else None, len(arr), None, 0, None)
+
+
+@pytest.mark.parametrize("kw,msg", [
+    (dict(N=601), "F*R*C"),
+    (dict(anchors=(7, 2)), "ascending"),
+    (dict(anchors=(2, 2)), "ascending"),
+    (dict(anchors=(2, 10)), "outside"),
+    (dict(anchors=()), "anchor"),
+    (dict(d=32), "d = 32"),
+])
+def test_anchor_rejects(kw, msg):
+    assert _anchor(**kw) == INVALID
+    assert msg in cal.last_error()
+
+
+def test_dispatch_rejects_missing_flags_and_bad_anchors():
+    view = _view()
+    st = lib.calibatt_layer_dispatch(P, P, P, P, None, 2, 1000, 128, cal.BF16, 0.088, ctypes.byref(view), 0, 0,
+                                     None, 10, 10, 10, None, 0, None)
+    assert st == INVALID and "rep_flags" in cal.last_error()
+    flags = np.array([[[0, 1]]], dtype=np.uint8)
+    anchors = np.array([3], dtype=np.int32)
+    st = lib.calibatt_layer_dispatch(P, P, P, P, None, 2, 1000, 128, cal.BF16, 0.088, ctypes.byref(view), 0, 0,
+                                     flags.ctypes.data, 10, 10, 11, anchors.ctypes.data, 1, None)
+    assert st == INVALID and "F*R*C" in cal.last_error()
+
+
+def test_compile_rejects():
+    nnz = ctypes.c_int64(-1)
+    assert lib.calibatt_compile_skiplist(None, 1, 1, 1, 100, 10, P, None, 0, None, ctypes.byref(nnz), None) == INVALID
+    assert lib.calibatt_compile_skiplist(P, 1, 0, 1, 100, 10, P, None, 0, None, ctypes.byref(nnz), None) == INVALID
+    assert lib.calibatt_compile_skiplist(P, 1, 1, 1, 10**6, 1, P, None, 0, None, ctypes.byref(nnz), None) == INVALID
+    assert "exceeds" in cal.last_error()
+    assert lib.calibatt_compile_skiplist(P, 1, 1, 1, 100, 10, P, P, -1, None, ctypes.byref(nnz), None) == INVALID
+    assert lib.calibatt_compile_skiplist(P, 1, 1, 1, 100, 10, P, None, 0, None, None, None) == INVALID
+
+
+def test_product_path_does_not_import_the_oracle():
+    import sys
+    pkg = os.path.join(ROOT, "calibrated_block_sparse_skiplist_amd")
+    for dirpath, _, files in os.walk(pkg):
+        for f in files:
+            if f.endswith((".py", ".hip", ".h", ".cpp")):
+                src = open(os.path.join(dirpath, f)).read()
+                assert not re.search(r"\boracle\b", src.replace("the oracle", "")), f

@@ -1,0 +1,262 @@
+"""GPU attention parity against the fp64 oracle, through the C ABI.
+
+Tolerances (max |GPU - oracle| over every compared element): 1e-2 for bf16
+inputs, 1e-4 for fp32 inputs; lse 1e-3 / 1e-5. Small cases compare every
+element and span several tiles plus a ragged tail; the full Wan-shaped layers
+compare sampled query blocks and frames that the oracle evaluates one by one.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+import calibrated_block_sparse_skiplist_amd as cal
+from _gpu_util import (TOL_BF16, TOL_F32, TOL_LSE_BF16, TOL_LSE_F32, alloc_out, exact_values, host64,
+                       max_abs, random_qkv, say, to_device)
+
+pytestmark = pytest.mark.gpu
+
+
+def _tols(dtype):
+    return (TOL_BF16, TOL_LSE_BF16) if dtype == "bf16" else (TOL_F32, TOL_LSE_F32)
+
+
+def _masks(H, nb, p, seed, empty_row=True):
+    rng = np.random.default_rng(seed)
+    m = (rng.random((1, 1, H, nb, nb)) < p)
+    for h in range(H):
+        np.fill_diagonal(m[0, 0, h], True)
+    if empty_row and H > 1 and nb > 1:
+        m[0, 0, 1, nb // 2] = False
+    return m.astype(np.uint8)
+
+
+def _compile(masks, N, B):
+    return cal.compile_skiplist(torch.from_numpy(masks).cuda(), N, B)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("N,d,B", [(1000, 128, 128), (1000, 64, 128), (700, 128, 64), (700, 64, 64),
+                                   (128, 128, 128), (77, 128, 128), (300, 64, 64)])
+def test_block_sparse_small(dtype, N, d, B):
+    say(f"[sparse] dtype={dtype} N={N} d={d} B={B}")
+    H = 3
+    nb = -(-N // B)
+    q, k, v = random_qkv(H, N, d, dtype, seed=N + d + B)
+    masks = _masks(H, nb, 0.4, seed=N * d)
+    sl = _compile(masks, N, B)
+    o, lse = alloc_out(H, N, d, dtype)
+    scale = float(np.float32(1.0 / np.sqrt(d)))
+    cal.calibatt_block_sparse_attn(to_device(q, dtype), to_device(k, dtype), to_device(v, dtype), o, lse, sl, 0, 0,
+                                   scale=scale)
+    torch.cuda.synchronize()
+    rp, ci, _ = oracle.compile_skiplist(masks)
+    tol, tol_lse = _tols(dtype)
+    og, lg = host64(o), lse.cpu().numpy()
+    for h in range(H):
+        want_o, want_l = oracle.block_sparse_head(exact_values(q[h], dtype), exact_values(k[h], dtype),
+                                                  exact_values(v[h], dtype), rp, ci, h, B, scale)
+        assert max_abs(og[h], want_o) <= tol, (h, max_abs(og[h], want_o))
+        assert max_abs(lg[h], want_l) <= tol_lse, (h, max_abs(lg[h], want_l))
+    if nb > 1:   # the empty row of head 1 gives zeros and -inf
+        r = nb // 2
+        assert np.all(og[1, r * B:min((r + 1) * B, N)] == 0.0)
+        assert np.all(np.isneginf(lg[1, r * B:min((r + 1) * B, N)]))
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("F,R,C,anchors", [(3, 10, 20, [2, 7]), (2, 16, 16, [4, 12]), (2, 5, 30, [0, 1, 2, 3, 4]),
+                                           (4, 9, 7, [4])])
+def test_anchor_small(dtype, d, F, R, C, anchors):
+    say(f"[anchor] dtype={dtype} d={d} F={F} R={R} C={C} anchors={anchors}")
+    H = 2
+    N = F * R * C
+    q, k, v = random_qkv(H, N, d, dtype, seed=N + d + len(anchors))
+    o, lse = alloc_out(H, N, d, dtype)
+    scale = float(np.float32(1.0 / np.sqrt(d)))
+    cal.calibatt_anchor_attn(to_device(q, dtype), to_device(k, dtype), to_device(v, dtype), o, lse, F, R, C, anchors,
+                             scale=scale)
+    torch.cuda.synchronize()
+    tol, tol_lse = _tols(dtype)
+    og, lg = host64(o), lse.cpu().numpy()
+    for h in range(H):
+        want_o, want_l = oracle.anchor_head(exact_values(q[h], dtype), exact_values(k[h], dtype),
+                                            exact_values(v[h], dtype), F, R, C, anchors, scale)
+        assert max_abs(og[h], want_o) <= tol
+        assert max_abs(lg[h], want_l) <= tol_lse
+
+
+def test_tiny_config_layer_dispatch_fp32():
+    wl = workloads.make_workload("tiny")
+    cfg = wl.cfg
+    say(f"[dispatch] {cfg.title}")
+    sl = _compile(wl.masks, cfg.N, cfg.B)
+    o, lse = alloc_out(cfg.H, cfg.N, cfg.d, "f32")
+    cal.calibatt_layer_dispatch(to_device(wl.q, "f32"), to_device(wl.k, "f32"), to_device(wl.v, "f32"), o, lse, sl,
+                                0, 0, wl.rep_flags, cfg.F, cfg.R, cfg.C, wl.anchors, scale=wl.scale)
+    torch.cuda.synchronize()
+    rp, ci, _ = oracle.compile_skiplist(wl.masks)
+    want_o, want_l = oracle.layer_forward(wl.q, wl.k, wl.v, rp, ci, cfg.T, cfg.L, cfg.H, cfg.B, 0, 0, wl.rep_flags,
+                                          cfg.F, cfg.R, cfg.C, wl.anchors, wl.scale)
+    assert max_abs(host64(o), want_o) <= TOL_F32
+    assert max_abs(lse.cpu().numpy(), want_l) <= TOL_LSE_F32
+
+
+@pytest.mark.parametrize("dtype,d,B", [("bf16", 128, 128), ("bf16", 64, 64), ("f32", 64, 64)])
+def test_dispatch_small_mixed(dtype, d, B):
+    say(f"[dispatch] mixed dtype={dtype} d={d} B={B}")
+    H, F, R, C = 4, 2, 12, 40
+    N = F * R * C
+    nb = -(-N // B)
+    q, k, v = random_qkv(H, N, d, dtype, seed=99 + d)
+    masks = _masks(H, nb, 0.3, seed=5 + d)
+    flags = np.array([[[0, 1, 0, 1]]], dtype=np.uint8)
+    anchors = [2, 6, 10]
+    sl = _compile(masks, N, B)
+    o, lse = alloc_out(H, N, d, dtype)
+    scale = float(np.float32(1.0 / np.sqrt(d)))
+    cal.calibatt_layer_dispatch(to_device(q, dtype), to_device(k, dtype), to_device(v, dtype), o, lse, sl, 0, 0, flags,
+                                F, R, C, anchors, scale=scale)
+    torch.cuda.synchronize()
+    rp, ci, _ = oracle.compile_skiplist(masks)
+    want_o, want_l = oracle.layer_forward(exact_values(q, dtype), exact_values(k, dtype), exact_values(v, dtype),
+                                          rp, ci, 1, 1, H, B, 0, 0, flags, F, R, C, anchors, scale)
+    tol, tol_lse = _tols(dtype)
+    assert max_abs(host64(o), want_o) <= tol
+    assert max_abs(lse.cpu().numpy(), want_l) <= tol_lse
+
+
+def test_head_subset_leaves_other_heads_untouched():
+    H, N, d, B = 4, 500, 128, 128
+    q, k, v = random_qkv(H, N, d, "bf16", seed=3)
+    masks = _masks(H, -(-N // B), 0.5, seed=4)
+    sl = _compile(masks, N, B)
+    o, lse = alloc_out(H, N, d, "bf16")
+    cal.calibatt_block_sparse_attn(to_device(q, "bf16"), to_device(k, "bf16"), to_device(v, "bf16"), o, lse, sl, 0,
+                                   0, heads=[2, 0])
+    torch.cuda.synchronize()
+    og = host64(o)
+    assert np.all(np.isnan(og[1])) and np.all(np.isnan(og[3]))
+    assert np.all(np.isfinite(og[0])) and np.all(np.isfinite(og[2]))
+
+
+def test_deterministic_and_perturbation_invariant():
+    # Rows whose lists skip block c do not change when K/V of block c change;
+    # NaN written into never-kept key blocks never reaches any output.
+    H, N, d, B = 2, 1000, 128, 128
+    nb = -(-N // B)
+    q, k, v = random_qkv(H, N, d, "bf16", seed=11)
+    masks = _masks(H, nb, 0.35, seed=12, empty_row=False)
+    masks[0, 0, :, :, 3] = 0          # key block 3 never kept...
+    masks[0, 0, :, 3, 3] = 1          # ...except on its own diagonal
+    sl = _compile(masks, N, B)
+    qd, kd, vd = to_device(q, "bf16"), to_device(k, "bf16"), to_device(v, "bf16")
+    o1, l1 = alloc_out(H, N, d, "bf16")
+    o2, l2 = alloc_out(H, N, d, "bf16")
+    cal.calibatt_block_sparse_attn(qd, kd, vd, o1, l1, sl, 0, 0)
+    cal.calibatt_block_sparse_attn(qd, kd, vd, o2, l2, sl, 0, 0)
+    torch.cuda.synchronize()
+    assert torch.equal(o1.view(torch.int16), o2.view(torch.int16)) and torch.equal(l1, l2)
+    # perturb K and V of block 5 for head 0
+    kd2, vd2 = kd.clone(), vd.clone()
+    kd2[0, 5 * B:6 * B] += 1.0
+    vd2[0, 5 * B:6 * B] -= 2.0
+    o3, l3 = alloc_out(H, N, d, "bf16")
+    cal.calibatt_block_sparse_attn(qd, kd2, vd2, o3, l3, sl, 0, 0)
+    torch.cuda.synchronize()
+    for r in range(nb):
+        rows = slice(r * B, min((r + 1) * B, N))
+        same = torch.equal(o3[0, rows].view(torch.int16), o1[0, rows].view(torch.int16))
+        assert same == (masks[0, 0, 0, r, 5] == 0), r
+    assert torch.equal(o3[1].view(torch.int16), o1[1].view(torch.int16))
+    # NaN in block 3 (kept only by query block 3): every other row stays finite and unchanged
+    kd3, vd3 = kd.clone(), vd.clone()
+    kd3[:, 3 * B:4 * B] = float("nan")
+    vd3[:, 3 * B:4 * B] = float("nan")
+    o4, l4 = alloc_out(H, N, d, "bf16")
+    cal.calibatt_block_sparse_attn(qd, kd3, vd3, o4, l4, sl, 0, 0)
+    torch.cuda.synchronize()
+    keep = torch.ones(N, dtype=torch.bool)
+    keep[3 * B:4 * B] = False
+    assert torch.equal(o4[:, keep].view(torch.int16), o1[:, keep].view(torch.int16))
+
+
+def test_anchor_output_ignores_non_anchor_queries():
+    H, F, R, C, d = 1, 3, 9, 50, 128
+    N = F * R * C
+    anchors = [1, 4, 7]
+    q, k, v = random_qkv(H, N, d, "bf16", seed=21)
+    o1, l1 = alloc_out(H, N, d, "bf16")
+    cal.calibatt_anchor_attn(to_device(q, "bf16"), to_device(k, "bf16"), to_device(v, "bf16"), o1, l1, F, R, C,
+                             anchors)
+    q2 = q.copy().reshape(H, F, R, C, d)
+    other = [r for r in range(R) if r not in anchors]
+    q2[:, :, other] = workloads.bf16_bits(np.random.default_rng(1).standard_normal(q2[:, :, other].shape,
+                                                                                  dtype=np.float32) * 10)
+    o2, l2 = alloc_out(H, N, d, "bf16")
+    cal.calibatt_anchor_attn(to_device(q2.reshape(H, N, d), "bf16"), to_device(k, "bf16"), to_device(v, "bf16"), o2,
+                             l2, F, R, C, anchors)
+    torch.cuda.synchronize()
+    assert torch.equal(o1.view(torch.int16), o2.view(torch.int16))
+    assert torch.equal(l1, l2)
+
+
+# ---------------------------------------------------------------------------
+# Full-size Wan-shaped layers, launched exactly as the benchmark launches them
+# (calibatt_layer_dispatch), checked on sampled query blocks and frames.
+# ---------------------------------------------------------------------------
+def _full_layer_check(key, n_sparse_heads=3, n_blocks=4, n_anchor_heads=2):
+    wl = workloads.make_workload(key)
+    cfg = wl.cfg
+    say(f"[full] {cfg.title}: H={cfg.H} N={cfg.N} d={cfg.d}")
+    sl = _compile(wl.masks, cfg.N, cfg.B)
+    q, k, v = (to_device(x, "bf16") for x in (wl.q, wl.k, wl.v))
+    o, lse = alloc_out(cfg.H, cfg.N, cfg.d, "bf16")
+    cal.calibatt_layer_dispatch(q, k, v, o, lse, sl, 0, 0, wl.rep_flags, cfg.F, cfg.R, cfg.C, wl.anchors,
+                                scale=wl.scale)
+    torch.cuda.synchronize()
+    assert torch.isfinite(o).all() and torch.isfinite(lse).all()
+    rp, ci, _ = oracle.compile_skiplist(wl.masks)
+    rng = np.random.default_rng(77)
+    flags = wl.rep_flags[0, 0]
+    sparse = [h for h in range(cfg.H) if not flags[h]]
+    rep = [h for h in range(cfg.H) if flags[h]]
+    counts = np.diff(rp)
+    for h in rng.choice(sparse, size=min(n_sparse_heads, len(sparse)), replace=False):
+        base = h * cfg.nb
+        heavy = int(np.argmax(counts[base:base + cfg.nb]))
+        blocks = sorted({0, cfg.nb - 1, heavy, *rng.choice(cfg.nb, size=n_blocks, replace=False).tolist()})
+        want_o, want_l = oracle.block_sparse_head(workloads.bf16_to_f32(wl.q[h]), workloads.bf16_to_f32(wl.k[h]),
+                                                  workloads.bf16_to_f32(wl.v[h]), rp, ci, int(h), cfg.B, wl.scale,
+                                                  blocks=blocks)
+        rows = np.concatenate([np.arange(b * cfg.B, min((b + 1) * cfg.B, cfg.N)) for b in blocks])
+        og = o[h, torch.from_numpy(rows).cuda()].float().cpu().numpy()
+        err = max_abs(og, want_o[rows])
+        say(f"  sparse head {h} blocks {blocks}: max err {err:.2e}")
+        assert err <= TOL_BF16
+        assert max_abs(lse[h, torch.from_numpy(rows).cuda()].cpu().numpy(), want_l[rows]) <= TOL_LSE_BF16
+    for h in (rng.choice(rep, size=min(n_anchor_heads, len(rep)), replace=False) if rep else []):
+        frames = sorted({0, cfg.F - 1, int(rng.integers(cfg.F))})
+        want_o, want_l = oracle.anchor_head(workloads.bf16_to_f32(wl.q[h]), workloads.bf16_to_f32(wl.k[h]),
+                                            workloads.bf16_to_f32(wl.v[h]), cfg.F, cfg.R, cfg.C, wl.anchors,
+                                            wl.scale, frames=frames)
+        rows = np.concatenate([np.arange(f * cfg.R * cfg.C, (f + 1) * cfg.R * cfg.C) for f in frames])
+        og = o[h, torch.from_numpy(rows).cuda()].float().cpu().numpy()
+        err = max_abs(og, want_o[rows])
+        say(f"  anchor head {h} frames {frames}: max err {err:.2e}")
+        assert err <= TOL_BF16
+        assert max_abs(lse[h, torch.from_numpy(rows).cuda()].cpu().numpy(), want_l[rows]) <= TOL_LSE_BF16
+
+
+def test_full_wan480_all_sparse():
+    _full_layer_check("wan480_sparse")
+
+
+def test_full_wan480_dual_path():
+    _full_layer_check("wan480_dual")
+
+
+def test_full_wan720_dual_path():
+    _full_layer_check("wan720")

@@ -1,0 +1,81 @@
+"""GPU skip-list compilation: bit-exact against the oracle (row_ptr, col_idx, order)."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+import calibrated_block_sparse_skiplist_amd as cal
+from _gpu_util import say
+
+pytestmark = pytest.mark.gpu
+
+
+def _compile_and_compare(masks: np.ndarray, N: int, B: int, label: str):
+    say(f"[skiplist] {label}: masks {masks.shape}")
+    T, L, H, nb, _ = masks.shape
+    dm = torch.from_numpy(np.ascontiguousarray(masks)).cuda()
+    sl = cal.compile_skiplist(dm, N, B)
+    torch.cuda.synchronize()
+    rp, ci, order = oracle.compile_skiplist(masks)
+    assert sl.nnz == int(rp[-1])
+    np.testing.assert_array_equal(sl.row_ptr.cpu().numpy(), rp)
+    np.testing.assert_array_equal(sl.col_idx.cpu().numpy()[:sl.nnz], ci)
+    np.testing.assert_array_equal(sl.order.cpu().numpy(), order)
+    return sl
+
+
+@pytest.mark.parametrize("shape,p,seed", [
+    ((1, 1, 1, 1), 1.0, 0), ((1, 1, 1, 1), 0.0, 1), ((1, 1, 2, 3), 0.5, 2), ((2, 3, 2, 7), 0.4, 3),
+    ((1, 1, 3, 64), 0.3, 4), ((1, 1, 2, 65), 0.7, 5), ((1, 2, 5, 131), 0.2, 6), ((3, 1, 2, 300), 0.05, 7),
+    ((1, 1, 1, 1030), 0.5, 8),
+])
+def test_random_masks(shape, p, seed):
+    rng = np.random.default_rng(seed)
+    T, L, H, nb = shape
+    masks = (rng.random((T, L, H, nb, nb)) < p).astype(np.uint8)
+    masks[masks == 1] = rng.integers(1, 256, size=int(masks.sum()), dtype=np.uint8)
+    if nb > 2:
+        masks[0, 0, 0, 1] = 0          # an empty row
+        masks[0, 0, -1, -1] = 7        # a full row
+    _compile_and_compare(masks, nb * 16, 16, f"random {shape} p={p}")
+
+
+def test_all_zero_dictionary_has_no_entries():
+    masks = np.zeros((1, 2, 3, 40, 40), np.uint8)
+    sl = _compile_and_compare(masks, 40 * 64, 64, "all zero")
+    assert sl.nnz == 0
+
+
+def test_many_segments_scan():
+    # rows = 2*4*5*300 = 12000 > several scan segments of 1024 rows
+    rng = np.random.default_rng(9)
+    masks = (rng.random((2, 4, 5, 300, 300)) < 0.1).astype(np.uint8)
+    _compile_and_compare(masks, 300 * 128 - 50, 128, "multi-segment")
+
+
+@pytest.mark.parametrize("key", ["tiny", "wan480_sparse", "wan720"])
+def test_config_masks(key):
+    wl = workloads.make_workload(key, with_data=False)
+    _compile_and_compare(wl.masks, wl.cfg.N, wl.cfg.B, key)
+
+
+def test_dictionary_480p_68():
+    cfg, masks, _ = workloads.make_dictionary_workload(0.68, 0.25, L=8, H=40)
+    _compile_and_compare(masks, cfg.N, cfg.B, "480p dictionary, 8 layers")
+
+
+def test_size_query_and_capacity_error():
+    rng = np.random.default_rng(10)
+    masks = (rng.random((1, 1, 2, 20, 20)) < 0.5).astype(np.uint8)
+    dm = torch.from_numpy(masks).cuda()
+    rp = torch.empty(2 * 20 + 1, dtype=torch.int64, device="cuda")
+    nnz = cal.calibatt_compile_skiplist(dm, 1, 1, 2, 20 * 64, 64, rp, None, 0, None)
+    assert nnz == int(masks.sum())
+    small = torch.full((nnz - 1,), -5, dtype=torch.int32, device="cuda")
+    with pytest.raises(cal.CalibattError) as ei:
+        cal.calibatt_compile_skiplist(dm, 1, 1, 2, 20 * 64, 64, rp, small, small.numel(), None)
+    assert ei.value.status == 2
+    assert torch.all(small == -5)          # nothing written on CAPACITY
+    want_rp, _, _ = oracle.compile_skiplist(masks)
+    np.testing.assert_array_equal(rp.cpu().numpy(), want_rp)
