@@ -1,0 +1,320 @@
+"""Benchmark of the CalibAtt layer hot path on one MI355X.
+
+One step = one pass of the whole hot path over one synthetic layer held in HBM:
+skip-list compilation of the layer's block masks (calibatt_compile_skiplist)
+followed by the per-head dual-path layer-call (calibatt_layer_dispatch: one
+attention launch covering block-sparse and anchor-row heads, then the anchor
+broadcast). W untimed warmup steps, then K timed steps bracketed by
+torch.cuda.synchronize().
+
+Default workload: a Wan-720p-shaped layer (H=40, N=75600 = 21x45x80 tokens,
+d=128, 128x128 blocks, bf16), 32 block-sparse heads at 68% mean sparsity
+(40-90% per head) and 8 repetitive heads with 5 anchor rows of 45.
+
+Printed: one JSON line with the metric (retained-block TFLOP/s), ms per step,
+the roofline of the dominant kernel (the attention kernel, timed per launch
+with HIP events on its stream), the same kernel run dense over all heads, and
+the CPU oracle timed on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2516.6     # MI355X dense bf16 MFMA: 256 CU x 2.4 GHz x 4096 FLOP/clk
+PEAK_HBM_GBS = 8000.0
+ATTN_KERNEL = "attn_bf16_kernel"
+ATTN_SOURCE = os.path.join(ROOT, "calibrated_block_sparse_skiplist_amd", "csrc", "attn_bf16.hip")
+
+
+def parse_args():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--config", default="wan720",
+                    choices=["tiny", "wan480_sparse", "wan480_dual", "wan720"])
+    ap.add_argument("--dense-reps", type=int, default=3, help="launches of the dense comparator")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0, help="budget of the CPU oracle sample")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-dense", action="store_true")
+    ap.add_argument("--copy-calib", action="store_true",
+                    help="only run a plain 1 GiB device copy (calibrates HBM byte counters)")
+    return ap.parse_args()
+
+
+# ---------------------------------------------------------------------------
+# algorithmic work (what the method must compute; exp and softmax not counted)
+# ---------------------------------------------------------------------------
+def block_sizes(N, B):
+    nb = -(-N // B)
+    s = np.full(nb, B, dtype=np.int64)
+    s[-1] = N - (nb - 1) * B
+    return s
+
+
+def sparse_head_flops(mask: np.ndarray, N: int, B: int, d: int) -> float:
+    """4 d sum over kept (r, c) of |I_r| |J_c|  (QK^T and PV, 2 FLOP per MAC)."""
+    s = block_sizes(N, B)
+    return float(4 * d * (s[:, None] * s[None, :] * (mask != 0)).sum())
+
+
+def anchor_head_flops(F, k, C, N, d) -> float:
+    return float(4 * d * F * k * C * N)
+
+
+def layer_work(wl):
+    cfg = wl.cfg
+    flags = wl.rep_flags[0, 0]
+    sparse = [h for h in range(cfg.H) if not flags[h]]
+    rep = [h for h in range(cfg.H) if flags[h]]
+    f_sparse = sum(sparse_head_flops(wl.masks[0, 0, h], cfg.N, cfg.B, cfg.d) for h in sparse)
+    f_anchor = len(rep) * anchor_head_flops(cfg.F, len(wl.anchors), cfg.C, cfg.N, cfg.d)
+    s = block_sizes(cfg.N, cfg.B)
+    tok = s[:, None] * s[None, :]
+    token_sp = [1.0 - float((tok * (wl.masks[0, 0, h] != 0)).sum()) / cfg.N ** 2 for h in sparse]
+    block_sp = [1.0 - float(wl.masks[0, 0, h].mean()) for h in sparse]
+    anchor_sp = 1.0 - len(wl.anchors) / cfg.R
+    layer_sp = (sum(token_sp) + anchor_sp * len(rep)) / cfg.H
+    dense = cfg.H * 4.0 * cfg.d * cfg.N * cfg.N
+    return dict(sparse_heads=sparse, rep_heads=rep, flops_sparse=f_sparse, flops_anchor=f_anchor,
+                flops=f_sparse + f_anchor, flops_dense=dense,
+                token_sparsity_sparse_heads=float(np.mean(token_sp)) if token_sp else None,
+                block_sparsity_sparse_heads=float(np.mean(block_sp)) if block_sp else None,
+                anchor_query_sparsity=anchor_sp if rep else None, layer_interaction_sparsity=layer_sp)
+
+
+# ---------------------------------------------------------------------------
+# CPU oracle baseline on a bounded sample
+# ---------------------------------------------------------------------------
+def cpu_baseline(wl, budget_s: float):
+    import oracle
+    import workloads
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        cores = 1
+    cfg = wl.cfg
+    rp, ci, _ = oracle.compile_skiplist(wl.masks)
+    flags = wl.rep_flags[0, 0]
+    sparse = [h for h in range(cfg.H) if not flags[h]]
+    rep = [h for h in range(cfg.H) if flags[h]]
+    rng = np.random.default_rng(123)
+    flops = 0.0
+    t_used = 0.0
+    n_blocks = 0
+    n_frames = 0
+    sizes = block_sizes(cfg.N, cfg.B)
+    as_f = workloads.bf16_to_f32 if cfg.dtype == "bf16" else (lambda x: x)
+    # one anchor frame first (if any), then random sparse query blocks until the budget is spent
+    if rep:
+        h = rep[0]
+        qh, kh, vh = as_f(wl.q[h]), as_f(wl.k[h]), as_f(wl.v[h])
+        t0 = time.perf_counter()
+        oracle.anchor_head(qh, kh, vh, cfg.F, cfg.R, cfg.C, wl.anchors, wl.scale, frames=[0])
+        t_used += time.perf_counter() - t0
+        flops += 4.0 * cfg.d * len(wl.anchors) * cfg.C * cfg.N
+        n_frames += 1
+    cache = {}
+    while t_used < budget_s and sparse:
+        h = int(rng.choice(sparse))
+        r = int(rng.integers(cfg.nb))
+        if h not in cache:
+            cache = {h: (as_f(wl.q[h]), as_f(wl.k[h]), as_f(wl.v[h]))}
+        qh, kh, vh = cache[h]
+        t0 = time.perf_counter()
+        oracle.block_sparse_head(qh, kh, vh, rp, ci, h, cfg.B, wl.scale, blocks=[r])
+        t_used += time.perf_counter() - t0
+        row = h * cfg.nb + r
+        cols = ci[rp[row]:rp[row + 1]]
+        flops += 4.0 * cfg.d * sizes[r] * float(sizes[cols].sum())
+        n_blocks += 1
+    value = flops / t_used / 1e12 if t_used > 0 else None
+    return {"value": value, "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"fp64 numpy oracle on {n_blocks} random block-sparse query blocks and {n_frames} anchor "
+                      f"frame(s) of the same layer: {flops / 1e12:.4f} TFLOP in {t_used:.1f} s",
+            "seconds": t_used, "tflop": flops / 1e12}
+
+
+def pmc_traffic(kernel_sha: str):
+    """HBM bytes per launch from the committed counter summary, if it matches this kernel source."""
+    path = os.path.join(ROOT, "profiles", "attn_wan720_hbm_counters.md")
+    if not os.path.exists(path):
+        return None
+    vals = {}
+    for line in open(path):
+        if ":" in line and line.strip().startswith("- "):
+            k, v = line.strip()[2:].split(":", 1)
+            vals[k.strip()] = v.strip()
+    if vals.get("kernel_source_sha256", "")[:16] != kernel_sha[:16]:
+        return None
+    try:
+        return float(vals["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def main():
+    args = parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(the layer shards by head with no communication; see the design notes)", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    if args.copy_calib:
+        src = torch.empty(1 << 28, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes_read": src.numel() * 4, "copy_bytes_written": src.numel() * 4}))
+        return
+
+    import workloads
+    import calibrated_block_sparse_skiplist_amd as cal
+
+    t0 = time.time()
+    wl = workloads.make_workload(args.config)
+    cfg = wl.cfg
+    work = layer_work(wl)
+    print(f"[bench] {cfg.title}: generated in {time.time() - t0:.1f} s", file=sys.stderr, flush=True)
+
+    dev = torch.device("cuda")
+    tdt = torch.bfloat16 if cfg.dtype == "bf16" else torch.float32
+
+    def up(x):
+        if cfg.dtype == "bf16":
+            return torch.from_numpy(x.view(np.int16)).view(torch.bfloat16).to(dev)
+        return torch.from_numpy(x).to(dev)
+
+    q, k, v = up(wl.q), up(wl.k), up(wl.v)
+    o = torch.empty_like(q)
+    lse = torch.empty((cfg.H, cfg.N), dtype=torch.float32, device=dev)
+    masks = torch.from_numpy(wl.masks).to(dev)
+    sl = cal.compile_skiplist(masks, cfg.N, cfg.B)
+    T, L, H, nb = 1, 1, cfg.H, cfg.nb
+    stream = torch.cuda.current_stream()
+
+    def step(ev_pair=None):
+        cal.calibatt_compile_skiplist(masks, T, L, H, cfg.N, cfg.B, sl.row_ptr, sl.col_idx, sl.col_idx.numel(),
+                                      sl.order, stream)
+        if ev_pair is not None:
+            cal.calibatt_set_kernel_events(ev_pair[0].cuda_event, ev_pair[1].cuda_event)
+        cal.calibatt_layer_dispatch(q, k, v, o, lse, sl, 0, 0, wl.rep_flags, cfg.F, cfg.R, cfg.C, wl.anchors,
+                                    scale=wl.scale, stream=stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    for a, b in evs:          # create the underlying HIP events
+        a.record(stream)
+        b.record(stream)
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    for i in range(args.steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_start
+    ms_per_step = wall * 1e3 / args.steps
+    kernel_ms = [a.elapsed_time(b) for a, b in evs]
+    attn_ms = float(np.mean(kernel_ms))
+
+    # layer-call alone (no compile), for reference
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    reps = max(3, args.steps // 2)
+    for _ in range(reps):
+        cal.calibatt_layer_dispatch(q, k, v, o, lse, sl, 0, 0, wl.rep_flags, cfg.F, cfg.R, cfg.C, wl.anchors,
+                                    scale=wl.scale, stream=stream)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    layer_ms = e0.elapsed_time(e1) / reps
+    # compile alone
+    t_c = time.perf_counter()
+    for _ in range(5):
+        cal.calibatt_compile_skiplist(masks, T, L, H, cfg.N, cfg.B, sl.row_ptr, sl.col_idx, sl.col_idx.numel(),
+                                      sl.order, stream)
+    torch.cuda.synchronize()
+    compile_ms = (time.perf_counter() - t_c) * 1e3 / 5
+
+    dense_ms = None
+    if not args.no_dense:
+        ones = torch.ones((1, 1, H, nb, nb), dtype=torch.uint8, device=dev)
+        sld = cal.compile_skiplist(ones, cfg.N, cfg.B)
+        od = torch.empty_like(q)
+        cal.calibatt_block_sparse_attn(q, k, v, od, None, sld, 0, 0, scale=wl.scale, stream=stream)
+        torch.cuda.synchronize()
+        d_ms = []
+        for _ in range(args.dense_reps):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            b.record(stream)
+            cal.calibatt_set_kernel_events(a.cuda_event, b.cuda_event)
+            cal.calibatt_block_sparse_attn(q, k, v, od, None, sld, 0, 0, scale=wl.scale, stream=stream)
+            torch.cuda.synchronize()
+            d_ms.append(a.elapsed_time(b))
+        dense_ms = float(np.mean(d_ms))
+        del od, sld, ones
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(wl, args.cpu_seconds)
+
+    flops = work["flops"]
+    achieved = flops / (attn_ms * 1e-3) / 1e12
+    sha = hashlib.sha256(open(ATTN_SOURCE, "rb").read()).hexdigest()
+    traffic = pmc_traffic(sha)
+    value = flops / (ms_per_step * 1e-3) / 1e12
+    res = {
+        "metric": "ms per attention layer-call + retained-block TFLOP/s (% of bf16 MFMA peak)",
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 3),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": cfg.dtype,
+        "data": "synthetic",
+        "config": {"workload": f"{cfg.key}: {cfg.title}", "H": cfg.H, "N": cfg.N, "d": cfg.d, "B": cfg.B,
+                   "frames_rows_cols": [cfg.F, cfg.R, cfg.C], "sparse_heads": len(work["sparse_heads"]),
+                   "repetitive_heads": len(work["rep_heads"]), "anchor_rows": [int(a) for a in wl.anchors],
+                   "step": "calibatt_compile_skiplist + calibatt_layer_dispatch"},
+        "pct_of_bf16_peak": round(100.0 * value / PEAK_BF16_TFLOPS, 2),
+        "layer_call_ms": round(layer_ms, 3),
+        "compile_ms": round(compile_ms, 3),
+        "attn_kernel_ms": round(attn_ms, 3),
+        "retained_tflop_per_layer": round(flops / 1e12, 3),
+        "tflop_sparse_heads": round(work["flops_sparse"] / 1e12, 3),
+        "tflop_anchor_heads": round(work["flops_anchor"] / 1e12, 3),
+        "dense_same_kernel_ms": round(dense_ms, 3) if dense_ms else None,
+        "dense_tflops": round(work["flops_dense"] / (dense_ms * 1e-3) / 1e12, 1) if dense_ms else None,
+        "speedup_vs_dense": round(dense_ms / layer_ms, 3) if dense_ms else None,
+        "sparsity": {"token_sparse_heads": work["token_sparsity_sparse_heads"],
+                     "block_sparse_heads": work["block_sparsity_sparse_heads"],
+                     "anchor_query": work["anchor_query_sparsity"],
+                     "layer_interactions": work["layer_interaction_sparsity"]},
+        "roofline": {"kernel": ATTN_KERNEL, "bound": "mfma", "achieved": round(achieved, 2),
+                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                     "traffic": traffic, "flop_per_launch": flops, "launch_ms": round(attn_ms, 3)},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -7,48 +7,67 @@
 // and every key block (same notes, Key Design 3).
 //
 // Work decomposition. One workgroup owns one work item: a tile of BLK queries
-// of one head. Its BLK/32 waves own 32 queries each. For every listed key
-// block the workgroup stages K and V (BLK x D bf16 each) in LDS and each wave
-//   1. computes S^T = K Q^T with v_mfma_f32_32x32x16_bf16 (A = K from LDS,
-//      B = Q^T held in registers), so every lane owns one query column and
-//      half of the keys: row maxima need one cross-lane exchange (lane ^ 32);
-//   2. runs the online softmax in fp32 (exp2 with log2(e) folded into the
-//      scale, running max and per-lane partial sums);
-//   3. accumulates O^T += V^T P^T with the same MFMA: A = V^T read from
-//      row-major LDS with ds_read_b64_tr_b16 (transposing 16-bit elements
-//      across 16-lane groups), B = P^T converted to bf16 straight from the
-//      S^T accumulators. The MFMA contraction index runs over keys in the
-//      order the accumulator layout produces; V is read in that same order.
-// The epilogue divides by the row sum and writes bf16 O (and fp32 lse).
+// of one head; its BLK/32 waves own 32 queries each. Two workgroups share a
+// CU (register budget capped at 256 per lane, 64 KB of LDS each), so one
+// workgroup's softmax overlaps the other's matrix work. For every listed key
+// block c each wave
+//   1. computes S^T = K_c Q^T with v_mfma_f32_32x32x16_bf16 (A = K from LDS,
+//      B = Q^T held in registers): every lane owns one query column and half
+//      of the keys, so a row maximum needs one exchange with lane ^ 32;
+//   2. runs the online softmax in fp32: exp2 with log2(e) folded into the
+//      scale, per-lane partial row sums, and a rescale of O only when some row
+//      maximum grows by more than 2^8 (the stale maximum is exact algebra:
+//      numerator and denominator share it);
+//   3. accumulates O^T += V_c^T P^T with the same MFMA: A = V^T read from
+//      row-major LDS by ds_read_b64_tr_b16 (16-bit transpose across 16-lane
+//      groups), B = P^T packed to bf16 straight from the S^T accumulators; the
+//      contraction runs over keys in the order the accumulator layout holds
+//      them, and V is read in that same order.
+// K and V tiles move HBM -> LDS with global_load_lds_dwordx4 (no register
+// staging). The next block's K is fetched while this block's softmax and PV
+// run, and the next V while the next S^T runs; s_waitcnt vmcnt plus a
+// workgroup barrier publish each tile.
 //
-// LDS rows of K and V are XOR-swizzled in 16-byte chunks so that the MFMA
-// operand reads of 32 consecutive keys (K) and of 4-key x 64-byte patches (V)
-// spread over the banks.
+// LDS rows are XOR-swizzled in 16-byte chunks: K by (row & 15), so the 16
+// rows of an MFMA operand read hit distinct banks; V by 4*(row & 3), so the
+// 8-row x 64-byte patch of a transposed read spreads over all banks.
 #include "internal.h"
 
 namespace calibatt {
 namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef unsigned short u16;
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 
-constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
+constexpr float kRescaleThreshold = 8.0f;   // log2 units: stale maxima are allowed 2^8 headroom
 
-// LDS chunk swizzles (chunk = 16 bytes; CPR chunks per row).
 template <int CPR>
 __device__ __forceinline__ int swz_k(int row) { return row & (CPR - 1); }
 template <int CPR>
-__device__ __forceinline__ int swz_v(int row) { return ((row & 3) << 1) & (CPR - 1); }
+__device__ __forceinline__ int swz_v(int row) { return (4 * (row & 3)) & (CPR - 1); }
+
+// s_waitcnt with only the vector-memory counter constrained (gfx9 encoding).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
 
 __device__ __forceinline__ uint4 ld_global16(const void* p) { return *reinterpret_cast<const uint4*>(p); }
 
-__device__ __forceinline__ bf16x8 as_bf16x8(uint4 v) {
-  bf16x8 r;
-  __builtin_memcpy(&r, &v, 16);
-  return r;
+template <typename T, typename S>
+__device__ __forceinline__ T bitcast(const S& s) {
+  static_assert(sizeof(T) == sizeof(S), "size");
+  T t;
+  __builtin_memcpy(&t, &s, sizeof(T));
+  return t;
 }
 
 struct Item {
@@ -100,23 +119,44 @@ __device__ __forceinline__ int query_token(const AttnParams& p, const Item& it, 
   return (f * p.R + p.anchors[ai]) * p.C + c;
 }
 
+// Issue this wave's share of the HBM -> LDS copy of one BLK x D tile. Each
+// instruction fills 64 consecutive 16-byte LDS slots; lane l fetches the global
+// chunk that the swizzle places in slot l. Rows past the sequence end are
+// clamped to a valid row (their scores are masked, their probabilities are 0).
+template <int D, int BLK, int NW, bool IS_V>
+__device__ __forceinline__ void issue_tile(const u16* head_base, int c, int N, uint4* lds, int wave, int lane) {
+  constexpr int CPR = D / 8;
+  constexpr int LPW = BLK * CPR / 64 / NW;     // load instructions per wave
+  constexpr int RPI = 64 / CPR;                // rows per instruction
+  const u16* tile = head_base + (int64_t)c * BLK * D;
+  const int last_row = N - 1 - c * BLK;
+  const int pos = lane % CPR;
+#pragma unroll
+  for (int i = 0; i < LPW; ++i) {
+    const int inst = wave * LPW + i;
+    const int row = inst * RPI + lane / CPR;
+    const int ch = pos ^ (IS_V ? swz_v<CPR>(row) : swz_k<CPR>(row));
+    const u16* src = tile + min(row, last_row) * D + ch * 8;
+    __builtin_amdgcn_global_load_lds(src, (lds_void*)(lds + inst * 64), 16, 0, 0);
+  }
+}
+
 template <int D, int BLK>
-__global__ __launch_bounds__(BLK * 2) void attn_bf16_kernel(const AttnParams p) {
+__global__ __launch_bounds__(BLK * 2) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void attn_bf16_kernel(const AttnParams p) {
   constexpr int NW = BLK / 32;           // waves per workgroup
-  constexpr int NT = NW * 64;            // threads
   constexpr int CPR = D / 8;             // 16-byte chunks per K/V row
   constexpr int KT = BLK / 32;           // 32-key tiles of S^T per block
   constexpr int DS = D / 16;             // 16-wide d slabs (QK contraction)
   constexpr int DT = D / 32;             // 32-wide d tiles of O^T
   constexpr int KS = BLK / 16;           // 16-key slabs (PV contraction)
-  static_assert(NT == BLK * 2, "one wave per 32 queries");
+  constexpr int LPW = BLK * CPR / 64 / NW;
 
   __shared__ uint4 lds_k[BLK * CPR];
   __shared__ uint4 lds_v[BLK * CPR];
 
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int h = lane >> 5;               // half of the wave
   const int l32 = lane & 31;
 
@@ -132,32 +172,39 @@ __global__ __launch_bounds__(BLK * 2) void attn_bf16_kernel(const AttnParams p) 
   for (int s = 0; s < DS; ++s) {
     uint4 raw = make_uint4(0, 0, 0, 0);
     if (qtok >= 0) raw = ld_global16(Q + (int64_t)qtok * D + 16 * s + 8 * h);
-    qf[s] = as_bf16x8(raw);
+    qf[s] = bitcast<bf16x8>(raw);
   }
 
   f32x16 oacc[DT];
 #pragma unroll
   for (int u = 0; u < DT; ++u) oacc[u] = f32x16{};
-  float m_run = -INFINITY;   // running max of scaled scores (log2 units)
+  float m_run = -INFINITY;   // reference maximum of scaled scores (log2 units)
   float l_run = 0.0f;        // this lane's partial sum of probabilities
 
   const int last_valid = p.N - (p.nb - 1) * BLK;   // tokens in the last block
 
+  if (it.n > 0) {
+    const int c0 = it.list ? it.list[0] : 0;
+    issue_tile<D, BLK, NW, false>(K, c0, p.N, lds_k, wave, lane);
+    issue_tile<D, BLK, NW, true>(V, c0, p.N, lds_v, wave, lane);
+  }
+
   for (int step = 0; step < it.n; ++step) {
     const int c = it.list ? it.list[step] : step;
+    // Lane-dependent LDS and tile addresses are rebuilt from an opaque copy of
+    // the lane id every iteration: hoisted out of the loop they would need
+    // ~30 extra registers and spill at two workgroups per CU.
+    int lo = lane;
+    asm volatile("" : "+v"(lo));
+    const int lo32 = lo & 31;
+    const int lh = lo >> 5;
+    const int g = lo >> 4;          // 16-lane group of the transposed reads
+    const int j = lo & 15;
+    const bool has_next = step + 1 < it.n;
+    const int cn = has_next ? (it.list ? it.list[step + 1] : step + 1) : 0;
 
-    // ---- stage K_c and V_c into LDS (row-major, chunk-swizzled) ----
-    __syncthreads();
-#pragma unroll
-    for (int i = 0; i < BLK * CPR / NT; ++i) {
-      const int pidx = tid + i * NT;
-      const int row = pidx / CPR;
-      const int ch = pidx % CPR;
-      const int grow = min(c * BLK + row, p.N - 1);
-      const int64_t goff = (int64_t)grow * D + ch * 8;
-      lds_k[row * CPR + (ch ^ swz_k<CPR>(row))] = ld_global16(K + goff);
-      lds_v[row * CPR + (ch ^ swz_v<CPR>(row))] = ld_global16(V + goff);
-    }
+    // ---- K_c resident (this wave's V_c loads may still be in flight) ----
+    wait_vmcnt<LPW>();
     __syncthreads();
 
     // ---- S^T = K Q^T ----
@@ -165,14 +212,16 @@ __global__ __launch_bounds__(BLK * 2) void attn_bf16_kernel(const AttnParams p) 
 #pragma unroll
     for (int t = 0; t < KT; ++t) {
       sacc[t] = f32x16{};
-      const int key = 32 * t + l32;
+      const int key = 32 * t + lo32;
 #pragma unroll
       for (int s = 0; s < DS; ++s) {
-        const int ch = 2 * s + h;
-        bf16x8 a = as_bf16x8(lds_k[key * CPR + (ch ^ swz_k<CPR>(key))]);
+        const int ch = 2 * s + lh;
+        bf16x8 a = bitcast<bf16x8>(lds_k[key * CPR + (ch ^ swz_k<CPR>(key))]);
         sacc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[s], sacc[t], 0, 0, 0);
       }
     }
+    __syncthreads();                              // every wave is done reading K_c
+    if (has_next) issue_tile<D, BLK, NW, false>(K, cn, p.N, lds_k, wave, lo);
 
     // ---- mask keys past N in a partial last block ----
     if (c == p.nb - 1 && last_valid < BLK) {
@@ -185,59 +234,66 @@ __global__ __launch_bounds__(BLK * 2) void attn_bf16_kernel(const AttnParams p) 
         }
     }
 
-    // ---- online softmax (fp32, log2 domain) ----
+    // ---- online softmax (fp32, log2 domain, lazy rescale) ----
     float mx = -INFINITY;
 #pragma unroll
     for (int t = 0; t < KT; ++t)
 #pragma unroll
       for (int a = 0; a < 16; ++a) mx = fmaxf(mx, sacc[t][a]);
     mx = fmaxf(mx, __shfl_xor(mx, 32));
-    const float m_new = fmaxf(m_run, mx * p.scale_log2);
-    const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);   // 0 on the first block
-    m_run = m_new;
+    const float mb = mx * p.scale_log2;
+    if (__ballot(mb > m_run + kRescaleThreshold) != 0) {
+      const float m_new = fmaxf(m_run, mb);
+      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);   // 0 while m_run is -inf
+      m_run = m_new;
+      l_run *= alpha;
+#pragma unroll
+      for (int u = 0; u < DT; ++u)
+#pragma unroll
+        for (int a = 0; a < 16; ++a) oacc[u][a] *= alpha;
+    }
+    const float neg_m = -m_run;
     float psum = 0.0f;
-    bf16x8 pf[KS];
+    uint32_t pk[KS][4];
 #pragma unroll
     for (int t = 0; t < KT; ++t)
 #pragma unroll
-      for (int a = 0; a < 16; ++a) {
-        const float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[t][a], p.scale_log2, -m_new));
-        psum += pv;
-        pf[2 * t + (a >> 3)][a & 7] = static_cast<__bf16>(pv);
+      for (int a = 0; a < 16; a += 2) {
+        const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[t][a], p.scale_log2, neg_m));
+        const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[t][a + 1], p.scale_log2, neg_m));
+        psum += p0;
+        psum += p1;
+        const bf16x2 two = __builtin_convertvector((f32x2){p0, p1}, bf16x2);
+        pk[2 * t + (a >> 3)][(a & 7) >> 1] = bitcast<uint32_t>(two);
       }
-    l_run = l_run * alpha + psum;
-#pragma unroll
-    for (int u = 0; u < DT; ++u)
-#pragma unroll
-      for (int a = 0; a < 16; ++a) oacc[u][a] *= alpha;
+    l_run += psum;
+
+    // ---- V_c resident ----
+    if (has_next) wait_vmcnt<LPW>(); else wait_vmcnt<0>();
+    __syncthreads();
 
     // ---- O^T += V^T P^T ----
 #pragma unroll
-    for (int u = 0; u < DT; ++u) {
+    for (int sl = 0; sl < KS; ++sl) {
+      const bf16x8 b = bitcast<bf16x8>(pk[sl]);
+      const int key_lo = 16 * sl + 4 * (g >> 1) + (j >> 2);
+      const int key_hi = key_lo + 8;
 #pragma unroll
-      for (int sl = 0; sl < KS; ++sl) {
-        const int g = lane >> 4;
-        const int j = lane & 15;
+      for (int u = 0; u < DT; ++u) {
         const int dcol = 32 * u + 16 * (g & 1) + 4 * (j & 3);
         const int ch = dcol >> 3;
         const int half = (dcol >> 2) & 1;
-        i16x4 lo, hi;
-        {
-          const int key = 16 * sl + 4 * (g >> 1) + (j >> 2);
-          const char* base = reinterpret_cast<const char*>(lds_v) + (key * CPR + (ch ^ swz_v<CPR>(key))) * 16 + half * 8;
-          lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)base);
-        }
-        {
-          const int key = 16 * sl + 8 + 4 * (g >> 1) + (j >> 2);
-          const char* base = reinterpret_cast<const char*>(lds_v) + (key * CPR + (ch ^ swz_v<CPR>(key))) * 16 + half * 8;
-          hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)base);
-        }
-        bf16x8 a;
-        __builtin_memcpy(&a, &lo, 8);
-        __builtin_memcpy(reinterpret_cast<char*>(&a) + 8, &hi, 8);
-        oacc[u] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf[sl], oacc[u], 0, 0, 0);
+        const char* base = reinterpret_cast<const char*>(lds_v);
+        const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (lds_i16x4*)(base + (key_lo * CPR + (ch ^ swz_v<CPR>(key_lo))) * 16 + half * 8));
+        const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (lds_i16x4*)(base + (key_hi * CPR + (ch ^ swz_v<CPR>(key_hi))) * 16 + half * 8));
+        struct { i16x4 lo, hi; } both = {lo, hi};
+        oacc[u] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bitcast<bf16x8>(both), b, oacc[u], 0, 0, 0);
       }
     }
+    __syncthreads();                              // every wave is done reading V_c
+    if (has_next) issue_tile<D, BLK, NW, true>(V, cn, p.N, lds_v, wave, lo);
   }
 
   // ---- epilogue ----
@@ -250,12 +306,11 @@ __global__ __launch_bounds__(BLK * 2) void attn_bf16_kernel(const AttnParams p) 
 #pragma unroll
       for (int g4 = 0; g4 < 4; ++g4) {
         const int d0 = 32 * u + 8 * g4 + 4 * h;
-        __bf16 vals[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) vals[i] = static_cast<__bf16>(oacc[u][4 * g4 + i] * inv);
-        uint2 packed;
-        __builtin_memcpy(&packed, vals, 8);
-        *reinterpret_cast<uint2*>(O + d0) = packed;
+        const bf16x2 v01 = __builtin_convertvector(
+            (f32x2){oacc[u][4 * g4 + 0] * inv, oacc[u][4 * g4 + 1] * inv}, bf16x2);
+        const bf16x2 v23 = __builtin_convertvector(
+            (f32x2){oacc[u][4 * g4 + 2] * inv, oacc[u][4 * g4 + 3] * inv}, bf16x2);
+        *reinterpret_cast<uint2*>(O + d0) = make_uint2(bitcast<uint32_t>(v01), bitcast<uint32_t>(v23));
       }
     if (p.lse && h == 0) {
       p.lse[(int64_t)it.head * p.N + qtok] = l_tot > 0.0f ? (m_run + __log2f(l_tot)) * kLn2 : -INFINITY;

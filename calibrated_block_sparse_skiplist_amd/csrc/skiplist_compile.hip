@@ -7,8 +7,8 @@
 // flattened (record, query block) pairs; lists are ascending.
 //
 // Passes (all integer work, so results are exact):
-//   1. count_scan: one wave per mask row counts nonzero bytes with ballots; each
-//      workgroup then scans its segment of kSeg rows into row_ptr[1 + row].
+//   1. count: one wave per mask row counts nonzero bytes with ballots into
+//      row_ptr[1 + row]; segment_scan then scans each segment of kSeg rows in place.
 //   2. scan_totals: one workgroup turns the segment-end values into a global
 //      inclusive scan.
 //   3. add_offsets: every segment but the first adds the previous segment's
@@ -62,23 +62,27 @@ __device__ void block_inclusive_scan(int64_t* vals, int n, int64_t* partial) {
   __syncthreads();
 }
 
-__global__ __launch_bounds__(kThreads) void count_scan_kernel(const uint8_t* __restrict__ masks,
-                                                              int64_t rows, int nb,
-                                                              int64_t* __restrict__ row_ptr) {
+// One wave per mask row: row_ptr[1 + row] = number of nonzero bytes.
+__global__ __launch_bounds__(kThreads) void count_kernel(const uint8_t* __restrict__ masks, int64_t rows, int nb,
+                                                         int64_t* __restrict__ row_ptr) {
+  const int lane = threadIdx.x & 63;
+  const int64_t row = (int64_t)blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6);
+  if (row >= rows) return;
+  const int cnt = row_count(masks + row * nb, nb, lane);
+  if (lane == 0) row_ptr[1 + row] = cnt;
+  if (row == 0 && lane == 0) row_ptr[0] = 0;
+}
+
+// In-place inclusive scan of each segment of kSeg counts.
+__global__ __launch_bounds__(kThreads) void segment_scan_kernel(int64_t rows, int64_t* __restrict__ row_ptr) {
   __shared__ int64_t vals[kSeg];
   __shared__ int64_t partial[kThreads];
-  const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
   const int64_t row0 = (int64_t)blockIdx.x * kSeg;
   const int n = (int)min<int64_t>(kSeg, rows - row0);
-  for (int i = wave; i < n; i += kThreads / 64) {
-    int cnt = row_count(masks + (row0 + i) * nb, nb, lane);
-    if (lane == 0) vals[i] = cnt;
-  }
+  for (int i = threadIdx.x; i < n; i += kThreads) vals[i] = row_ptr[1 + row0 + i];
   __syncthreads();
   block_inclusive_scan(vals, n, partial);
   for (int i = threadIdx.x; i < n; i += kThreads) row_ptr[1 + row0 + i] = vals[i];
-  if (blockIdx.x == 0 && threadIdx.x == 0) row_ptr[0] = 0;
 }
 
 __global__ __launch_bounds__(kThreads) void scan_totals_kernel(int64_t rows, int64_t* __restrict__ row_ptr) {
@@ -152,8 +156,12 @@ __global__ __launch_bounds__(kThreads) void order_kernel(const int64_t* __restri
 hipError_t launch_compile_count_scan(const uint8_t* masks, int64_t rows, int nb, int64_t* row_ptr,
                                      hipStream_t s) {
   const int64_t nseg = (rows + kSeg - 1) / kSeg;
-  hipLaunchKernelGGL(count_scan_kernel, dim3((unsigned)nseg), dim3(kThreads), 0, s, masks, rows, nb, row_ptr);
+  const int64_t grid = (rows + kThreads / 64 - 1) / (kThreads / 64);
+  hipLaunchKernelGGL(count_kernel, dim3((unsigned)grid), dim3(kThreads), 0, s, masks, rows, nb, row_ptr);
   hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(segment_scan_kernel, dim3((unsigned)nseg), dim3(kThreads), 0, s, rows, row_ptr);
+  e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (nseg > 1) {
     hipLaunchKernelGGL(scan_totals_kernel, dim3(1), dim3(kThreads), 0, s, rows, row_ptr);
