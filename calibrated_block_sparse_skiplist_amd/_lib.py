@@ -18,7 +18,7 @@ LIB_PATH = os.path.join(_HERE, "libcalibatt.so")
 
 OK, ERR_INVALID_ARG, ERR_CAPACITY, ERR_HIP, ERR_UNSUPPORTED = 0, 1, 2, 3, 4
 BF16, F32 = 0, 1
-MAX_HEADS, MAX_ANCHORS, MAX_NB = 256, 64, 8192
+MAX_HEADS, MAX_ANCHORS, MAX_NB = 256, 64, 4096
 
 EXPORTED = (
     "calibatt_compile_skiplist", "calibatt_block_sparse_attn", "calibatt_anchor_attn",

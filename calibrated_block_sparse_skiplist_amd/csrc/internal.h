@@ -16,8 +16,11 @@ namespace calibatt {
 //     (frame, anchor, column) order), visiting every key block;
 //   * block-sparse items follow: head sparse_heads[j / nb] visits the list of
 //     query block order[rec*nb + j % nb] (or j % nb when order is NULL).
-// The grid is therefore heaviest-first: anchor tiles see all nb key blocks,
-// and each head's query blocks come in descending kept count.
+// Anchor tiles (every key block) come first. Grid blocks map to items
+// XCD-aware: workgroups are dispatched round-robin over the 8 XCDs, so within
+// each run of 8 * xcd_group grid blocks XCD x receives xcd_group consecutive
+// items; neighbouring query blocks share most of their key blocks, which then
+// stay in that XCD's L2.
 struct AttnParams {
   const void* q;
   const void* k;
@@ -36,6 +39,8 @@ struct AttnParams {
   int64_t rec_row0;         // skip-list row of (t, l, head 0, block 0)
   int32_t rec_head_rows;    // rows per record (= nb)
   int32_t n_sparse;
+  int32_t use_order;        // 1: visit query blocks heaviest-first; 0: in block order
+  int32_t xcd_group;        // consecutive items given to one XCD (0: plain grid order)
   // anchor items
   int32_t n_anchor;
   int32_t anchor_tiles;

@@ -60,7 +60,7 @@ typedef enum { CALIBATT_BF16 = 0, CALIBATT_F32 = 1 } calibatt_dtype_t;
 /* Limits of one call. */
 #define CALIBATT_MAX_HEADS 256    /* heads taking part in one attention call */
 #define CALIBATT_MAX_ANCHORS 64   /* anchor rows per frame */
-#define CALIBATT_MAX_NB 8192      /* blocks per sequence */
+#define CALIBATT_MAX_NB 4096      /* blocks per sequence (N <= 4096 * B) */
 
 /*
  * A compiled skip-list dictionary (a POD view of caller-owned device arrays,
