@@ -49,6 +49,10 @@ def parse_args():
     ap.add_argument("--no-dense", action="store_true")
     ap.add_argument("--copy-calib", action="store_true",
                     help="only run a plain 1 GiB device copy (calibrates HBM byte counters)")
+    ap.add_argument("--dictionary-sweep", action="store_true",
+                    help="480p 40x40 dictionary: compile time and per-layer time over sparsity x "
+                         "repetitive fraction (one JSON line per point)")
+    ap.add_argument("--sweep-layers", type=int, default=4, help="layers timed per sweep point")
     return ap.parse_args()
 
 
@@ -164,6 +168,64 @@ def pmc_traffic(kernel_sha: str):
         return None
 
 
+def dictionary_sweep(args):
+    """Full-step mask dictionary at the 480p shape (40 layers x 40 heads): skip-list compile time
+    and per-layer attention time across sparsity {0, 50, 68, 85}% x repetitive fraction {0, 10, 25}%."""
+    import torch
+    import workloads
+    import calibrated_block_sparse_skiplist_amd as cal
+    base = workloads.get_config("wan480_dual")
+    q, k, v = workloads.make_qkv(base)
+    dev = torch.device("cuda")
+    qd, kd, vd = (torch.from_numpy(x.view(np.int16)).view(torch.bfloat16).to(dev) for x in (q, k, v))
+    o = torch.empty_like(qd)
+    anchors = workloads.equally_spaced_anchor_rows(base.R, base.n_anchor)
+    scale = float(np.float32(1.0 / np.sqrt(base.d)))
+    stream = torch.cuda.current_stream()
+    for sp in (0.0, 0.5, 0.68, 0.85):
+        for rf in (0.0, 0.10, 0.25):
+            cfg, masks, flags = workloads.make_dictionary_workload(sp, rf)
+            dm = torch.from_numpy(masks).to(dev)
+            sl = cal.compile_skiplist(dm, cfg.N, cfg.B)
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            reps = 3
+            for _ in range(reps):
+                cal.calibatt_compile_skiplist(dm, 1, cfg.L, cfg.H, cfg.N, cfg.B, sl.row_ptr, sl.col_idx,
+                                              sl.col_idx.numel(), sl.order, stream)
+            torch.cuda.synchronize()
+            compile_ms = (time.perf_counter() - t0) * 1e3 / reps
+            mask_bytes = masks.size
+            out_bytes = 4 * sl.nnz + 8 * (masks.shape[1] * masks.shape[2] * cfg.nb + 1) + 4 * masks.shape[1] * masks.shape[2] * cfg.nb
+            layer_ms, flops = [], 0.0
+            for l in range(min(args.sweep_layers, cfg.L)):
+                a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                cal.calibatt_layer_dispatch(qd, kd, vd, o, None, sl, 0, l, flags, cfg.F, cfg.R, cfg.C, anchors,
+                                            scale=scale, stream=stream)
+                a.record(stream)
+                cal.calibatt_layer_dispatch(qd, kd, vd, o, None, sl, 0, l, flags, cfg.F, cfg.R, cfg.C, anchors,
+                                            scale=scale, stream=stream)
+                b.record(stream)
+                torch.cuda.synchronize()
+                layer_ms.append(a.elapsed_time(b))
+                f = 0.0
+                for h in range(cfg.H):
+                    if flags[0, l, h]:
+                        f += anchor_head_flops(cfg.F, len(anchors), cfg.C, cfg.N, cfg.d)
+                    else:
+                        f += sparse_head_flops(masks[0, l, h], cfg.N, cfg.B, cfg.d)
+                flops += f / layer_ms[-1] / 1e9
+            print(json.dumps({"sweep": "wan480_dictionary", "sparsity_target": sp, "repetitive_fraction": rf,
+                              "layers": cfg.L, "heads": cfg.H, "nnz": sl.nnz,
+                              "block_sparsity": round(1.0 - float(masks.astype(np.float64).mean()), 4),
+                              "compile_ms": round(compile_ms, 3),
+                              "compile_GBps": round((2 * mask_bytes + out_bytes) / compile_ms / 1e6, 1),
+                              "layer_ms_mean": round(float(np.mean(layer_ms)), 3),
+                              "layer_ms": [round(x, 3) for x in layer_ms],
+                              "tflops_mean": round(flops / len(layer_ms), 1)}), flush=True)
+            del dm, sl
+
+
 def main():
     args = parse_args()
     if args.gpus != 1:
@@ -171,6 +233,9 @@ def main():
               "(the layer shards by head with no communication; see the design notes)", file=sys.stderr)
         sys.exit(2)
     import torch
+    if args.dictionary_sweep:
+        dictionary_sweep(args)
+        return
     if args.copy_calib:
         src = torch.empty(1 << 28, dtype=torch.float32, device="cuda")
         dst = torch.empty_like(src)

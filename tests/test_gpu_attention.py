@@ -260,3 +260,39 @@ def test_full_wan480_dual_path():
 
 def test_full_wan720_dual_path():
     _full_layer_check("wan720")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_dispatch_selects_records_by_timestep_and_layer(dtype):
+    # A T=2, L=3 dictionary with distinct masks and flags per record: every
+    # (t, l) layer-call must use exactly its own records.
+    T, L, H, F, R, C, d, B = 2, 3, 3, 2, 8, 32, 64, 64
+    N = F * R * C
+    nb = -(-N // B)
+    rng = np.random.default_rng(31)
+    masks = (rng.random((T, L, H, nb, nb)) < 0.3).astype(np.uint8)
+    for t in range(T):
+        for l in range(L):
+            for h in range(H):
+                np.fill_diagonal(masks[t, l, h], 1)
+    flags = (rng.random((T, L, H)) < 0.4).astype(np.uint8)
+    flags[0, 0] = [0, 1, 0]
+    flags[1, 2] = [1, 0, 1]
+    anchors = [1, 5]
+    q, k, v = random_qkv(H, N, d, dtype, seed=32)
+    sl = _compile(masks, N, B)
+    rp, ci, _ = oracle.compile_skiplist(masks)
+    qd, kd, vd = (to_device(x, dtype) for x in (q, k, v))
+    tol, tol_lse = _tols(dtype)
+    scale = float(np.float32(1.0 / np.sqrt(d)))
+    for t in range(T):
+        for l in range(L):
+            say(f"[dispatch] record t={t} l={l} flags={flags[t, l].tolist()}")
+            o, lse = alloc_out(H, N, d, dtype)
+            cal.calibatt_layer_dispatch(qd, kd, vd, o, lse, sl, t, l, flags, F, R, C, anchors, scale=scale)
+            torch.cuda.synchronize()
+            want_o, want_l = oracle.layer_forward(exact_values(q, dtype), exact_values(k, dtype),
+                                                  exact_values(v, dtype), rp, ci, T, L, H, B, t, l, flags,
+                                                  F, R, C, anchors, scale)
+            assert max_abs(host64(o), want_o) <= tol
+            assert max_abs(lse.cpu().numpy(), want_l) <= tol_lse
