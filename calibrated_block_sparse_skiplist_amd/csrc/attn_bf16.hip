@@ -8,26 +8,27 @@
 //
 // Work decomposition. One workgroup owns one work item: a tile of BLK queries
 // of one head; its BLK/32 waves own 32 queries each. Two workgroups share a
-// CU (register budget capped at 256 per lane, 64 KB of LDS each), so one
-// workgroup's softmax overlaps the other's matrix work. For every listed key
-// block c each wave
-//   1. computes S^T = K_c Q^T with v_mfma_f32_32x32x16_bf16 (A = K from LDS,
+// CU (register budget capped at 256 per lane, 64 KB of LDS each), so each
+// SIMD runs two waves that cover each other's waits. Keys are visited in
+// stages of 64 (two per 128-key block). In stage j each wave
+//   1. computes S^T_j = K_j Q^T with v_mfma_f32_32x32x16_bf16 (A = K from LDS,
 //      B = Q^T held in registers): every lane owns one query column and half
-//      of the keys, so a row maximum needs one exchange with lane ^ 32;
+//      of the stage's keys;
 //   2. runs the online softmax in fp32: exp2 with log2(e) folded into the
 //      scale, per-lane partial row sums of the bf16-rounded probabilities that
 //      also feed the PV product, and a rescale of O only when some row maximum
 //      grows by more than 2^8 (the stale maximum is exact algebra: numerator
 //      and denominator share it);
-//   3. accumulates O^T += V_c^T P^T with the same MFMA: A = V^T read from
-//      row-major LDS by ds_read_b64_tr_b16 (16-bit transpose across 16-lane
-//      groups), B = P^T packed to bf16 straight from the S^T accumulators; the
-//      contraction runs over keys in the order the accumulator layout holds
-//      them, and V is read in that same order.
+//   3. accumulates O^T += V_{j-1}^T P_{j-1}^T with the same MFMA, one stage
+//      behind: A = V^T read from row-major LDS by ds_read_b64_tr_b16 (16-bit
+//      transpose across 16-lane groups), B = P^T packed to bf16 straight from
+//      the S^T accumulators; the contraction runs over keys in the order the
+//      accumulator layout holds them, and V is read in that same order. The
+//      exponentials of step 2 are issued between these MFMAs, so the matrix
+//      pipe keeps running while the wave computes probabilities.
 // K and V tiles move HBM -> LDS with global_load_lds_dwordx4 (no register
-// staging). The next block's K is fetched while this block's softmax and PV
-// run, and the next V while the next S^T runs; s_waitcnt vmcnt plus a
-// workgroup barrier publish each tile.
+// staging), issued between the S^T MFMAs of the stage before they are used;
+// s_waitcnt vmcnt plus a workgroup barrier publish each tile.
 //
 // LDS rows are XOR-swizzled in 16-byte chunks: K by (row & 15), so the 16
 // rows of an MFMA operand read hit distinct banks; V by 4*(row & 3), so the
@@ -175,13 +176,15 @@ void attn_bf16_kernel(const AttnParams p) {
   constexpr int LPW = STAGE / 64 / NW;   // DMA instructions per wave, tensor and stage
   constexpr int RPI = 64 / CPR;          // rows per DMA instruction
 
-  // Two stages of K and of V (double buffer) and the item's key-block list.
-  // Each buffer is its own LDS object so that the compiler can see that reading
-  // one stage never aliases the DMA filling the other (otherwise it drains the
-  // DMA queue before every LDS read).
-  __shared__ uint4 lds_k0[STAGE], lds_k1[STAGE];
-  __shared__ uint4 lds_v0[STAGE], lds_v1[STAGE];
+  // Two stages of K and of V (double buffer) in one array, so that the
+  // buffer of an operand read is an immediate offset; and the item's
+  // key-block list.
+  __shared__ uint4 lds_kv[4 * STAGE];
   __shared__ uint16_t lds_list[kListCap];
+  uint4* const lds_k0 = lds_kv;
+  uint4* const lds_k1 = lds_kv + STAGE;
+  uint4* const lds_v0 = lds_kv + 2 * STAGE;
+  uint4* const lds_v1 = lds_kv + 3 * STAGE;
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -216,18 +219,16 @@ void attn_bf16_kernel(const AttnParams p) {
     qf[s] = bitcast<bf16x8>(raw);
   }
 
-  // DMA geometry of this lane: stage row and swizzled source chunk of each of
-  // its LPW instructions (byte offsets inside a stage of SUB rows).
-  uint32_t off_k[LPW], off_v[LPW];
-  int row_of[LPW];
-#pragma unroll
-  for (int i = 0; i < LPW; ++i) {
-    const int row = (wave * LPW + i) * RPI + lane / CPR;
-    const int pos = lane % CPR;
-    row_of[i] = row;
-    off_k[i] = (uint32_t)(row * D + (pos ^ swz_k<CPR>(row)) * 8) * 2u;
-    off_v[i] = (uint32_t)(row * D + (pos ^ swz_v<CPR>(row)) * 8) * 2u;
-  }
+  // DMA geometry. Copy instruction i of this wave fills the RPI stage rows
+  // from R = (wave*LPW + i)*RPI (uniform); lane l writes row R + q, q = l / CPR,
+  // chunk slot pos = l % CPR, with source chunk pos ^ swz(R + q). As R is a
+  // multiple of RPI and q < RPI, swz_k(R + q) = (R & (CPR-1)) ^ (q & (CPR-1))
+  // and swz_v(R + q) = swz_v(q): the byte offset of a lane is a fixed lane part,
+  // XORed (K only) with uniform chunk bits.
+  const int dq = lane / CPR;
+  const int dpos = lane % CPR;
+  const uint32_t dma_k_lane = (uint32_t)(dq * 2 * D + 16 * (dpos ^ (dq & (CPR - 1))));
+  const uint32_t dma_v_lane = (uint32_t)(dq * 2 * D + 16 * (dpos ^ swz_v<CPR>(dq)));
   __syncthreads();
 
   // Sources of the copy of stage `half` of key block c: a uniform base per
@@ -237,23 +238,30 @@ void attn_bf16_kernel(const AttnParams p) {
   // On the last block the base row is min(row0, N-1) and clamped lane offsets
   // are taken from it, so every offset stays non-negative (the 32-bit lane
   // offset of the copy instruction is unsigned).
-  struct StageSrc { const char* k; const char* v; bool clamp; int row0; int base_row; };
-  auto stage_src = [&](int c, int half) -> StageSrc {
+  struct StageSrc { const char* base; bool clamp; int row0; int base_row; };
+  auto stage_src = [&](const char* T, int c, int half) -> StageSrc {
     const int row0 = c * BLK + half * SUB;
     const int b0 = min(row0, n_tok - 1);
-    return {Kb + (int64_t)b0 * (D * 2), Vb + (int64_t)b0 * (D * 2), row0 + SUB > n_tok, row0, b0};
+    return {T + (int64_t)b0 * (D * 2), row0 + SUB > n_tok, row0, b0};
   };
-  // DMA instruction i (0 <= i < 2*LPW) of this wave for a stage: K first, then V.
-  auto issue_one = [&](const StageSrc& src, int i, uint4* lk, uint4* lv) {
-    const int ii = i % LPW;
-    uint32_t off = i < LPW ? off_k[ii] : off_v[ii];
-    if (src.clamp) {
-      const int grow = min(src.row0 + row_of[ii], n_tok - 1);
-      off = off - (uint32_t)(row_of[ii] * (D * 2)) + (uint32_t)((grow - src.base_row) * (D * 2));
+  // Copy instruction i (0 <= i < LPW) of this wave for one tensor of a stage.
+  auto issue_one = [&](const StageSrc& src, int i, bool is_k, uint4* dst_stage) {
+    const int r = (wave * LPW + i) * RPI;   // first stage row of the instruction
+    const uint32_t off = is_k ? dma_k_lane ^ (uint32_t)(16 * (r & (CPR - 1))) : dma_v_lane;
+    if (!src.clamp) {
+      dma16(src.base + (int64_t)r * (2 * D), off, dst_stage + (wave * LPW + i) * 64);
+    } else {
+      // (the empty statement keeps this rare path a branch instead of
+      // selects evaluated on every copy)
+      asm volatile("");
+      const int grow = min(src.row0 + r + dq, n_tok - 1);
+      const uint32_t coff = (uint32_t)((grow - src.base_row) * (2 * D)) + (off & (2 * D - 1));
+      dma16(src.base, coff, dst_stage + (wave * LPW + i) * 64);
     }
-    uint4* dst = (i < LPW ? lk : lv) + (wave * LPW + ii) * 64;
-    dma16(i < LPW ? src.k : src.v, off, dst);
   };
+
+  // Lane part of the K operand reads (see read_k).
+  const uint32_t k_lane = (uint32_t)(l32 * 2 * D + 16 * (h ^ (l32 & (CPR - 1))));
 
   // Key block visited at step i (uniform across the workgroup).
   auto block_at = [&](int i) -> int {
@@ -266,159 +274,202 @@ void attn_bf16_kernel(const AttnParams p) {
   float m_run = -INFINITY;   // reference maximum of scaled scores (log2 units)
   float l_run = 0.0f;        // this lane's partial sum of probabilities
 
+  // Software pipeline over 64-key stages. Stage j computes S^T_j and its
+  // probabilities P_j, while the matrix pipe runs the PV product of stage
+  // j-1: the exponentials of stage j are issued between those MFMAs. So K_j
+  // and V_{j-1} are read in stage j; the copy issued in stage j brings K_{j+1}
+  // and V_j. Two LDS buffers per tensor suffice: K_{j+1} overwrites K_{j-1},
+  // V_j overwrites V_{j-2}, and both were last read before the barrier that
+  // opens stage j. Stage 0 multiplies zero probabilities with a zeroed V
+  // buffer, so every stage runs the same code.
+  uint32_t pkA[KS][4], pkB[KS][4];   // bf16 P^T fragments of even / odd stages
+#pragma unroll
+  for (int i = 0; i < KS; ++i)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) pkB[i][e] = 0u;
+  for (int i = threadIdx.x; i < STAGE; i += NW * 64) lds_v1[i] = make_uint4(0, 0, 0, 0);
+
   const int n_stages = it.n * SPB;
   int c = n_stages > 0 ? block_at(0) : 0;
   if (n_stages > 0) {
-    const StageSrc src0 = stage_src(c, 0);
+    const StageSrc src0 = stage_src(Kb, c, 0);
 #pragma unroll
-    for (int i = 0; i < 2 * LPW; ++i) issue_one(src0, i, lds_k0, lds_v0);
+    for (int i = 0; i < LPW; ++i) issue_one(src0, i, true, lds_k0);
   }
 
-  // Stage j lives in buffer j & 1; the loop body is instantiated per buffer.
-  auto stage_body = [&](int j, const uint4* sk, const uint4* svv, uint4* nk, uint4* nv) {
+  // V^T operand of PV step idx (16-key slab sl, 32-wide d tile u) from a V
+  // stage. Lane (g = lane/16, jj = lane%16) reads keys 16*sl + vk and
+  // 16*sl + vk + 8, vk = 4*(g/2) + jj/4, at d = 32*u + 16*(g%2) + 4*(jj%4).
+  // The swizzle of those rows, 4*(vk & 3), has no bits below 4 and the chunk
+  // index is 4*u + (a part below 4), so the byte offset is a lane part XORed
+  // with 64*u; sl and the +8 rows are immediates.
+  const int g = lane >> 4;
+  const int jj = lane & 15;
+  const int vk = 4 * (g >> 1) + (jj >> 2);
+  const uint32_t v_lane = (uint32_t)(vk * 2 * D + 16 * (swz_v<CPR>(vk) + 2 * (g & 1) + ((jj & 3) >> 1)) +
+                                     8 * (jj & 1));
+  auto read_v = [&](const char* sv, int idx) -> bf16x8 {
+    const int sl = idx / DT, u = idx % DT;
+    const char* p = sv + 16 * sl * (2 * D) + (v_lane ^ (uint32_t)(64 * u));
+    struct { i16x4 lo, hi; } both;
+    both.lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)p);
+    both.hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p + 8 * (2 * D)));
+    return bitcast<bf16x8>(both);
+  };
+  // O^T += V^T P^T for one stage; `step(idx)` runs after PV MFMA idx (the
+  // exponentials of the next stage go there). Transposed reads run
+  // kPrefetchV MFMAs ahead.
+  auto pv_product = [&](const uint4* svv, const uint32_t (&pkp)[KS][4], auto step) {
+    const char* sv = reinterpret_cast<const char*>(svv);
+    bf16x8 ring[kPrefetchV];
+#pragma unroll
+    for (int i = 0; i < kPrefetchV; ++i) ring[i] = read_v(sv, i);
+#pragma unroll
+    for (int idx = 0; idx < KS * DT; ++idx) {
+      const int sl = idx / DT, u = idx % DT;
+      const bf16x8 a = ring[idx % kPrefetchV];
+      if (idx + kPrefetchV < KS * DT) ring[idx % kPrefetchV] = read_v(sv, idx + kPrefetchV);
+      oacc[u] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bitcast<bf16x8>(pkp[sl]), oacc[u], 0, 0, 0);
+      step(idx);
+      __builtin_amdgcn_sched_barrier(0);   // keep the interleaving as written
+    }
+  };
+  auto no_step = [](int) {};
+
+  // Stage j; the body is instantiated per parity of j, which fixes its buffers.
+  auto stage_body = [&](int j, const uint4* sk, uint4* nk, const uint4* svp, uint4* nv,
+                        const uint32_t (&pk_prev)[KS][4], uint32_t (&pk_cur)[KS][4]) {
     const int half = j % SPB;
     const bool has_next = j + 1 < n_stages;
     const int c_next = (has_next && half == SPB - 1) ? block_at(j / SPB + 1) : c;
 
-    // ---- stage j resident in every wave's view; the other buffer is free ----
+    // ---- K_j and V_{j-1} resident in every wave's view; the other buffers are free ----
     wait_vmcnt<0>();
     barrier_no_fence();
-    // The copy of stage j+1 is issued in small steps between the MFMAs below,
-    // so the address unit streams it while the matrix pipe works instead of
-    // every wave stalling on a burst right after the barrier.
-    const StageSrc nsrc = stage_src(has_next ? c_next : c, (j + 1) % SPB);
-
-    const int valid = n_tok - (c * BLK + half * SUB);   // keys of this stage inside the sequence
-    if (valid > 0) {
-      // Lane-dependent parts of the LDS operand addresses (loop-invariant; the
-      // compiler keeps them in registers, the per-step parts are immediates).
-      const int lo32 = l32;
-      const int lh = h;
-      const int g = lane >> 4;        // 16-lane group of the transposed reads
-      const int jj = lane & 15;
-      const char* sv = reinterpret_cast<const char*>(svv);
-
-      // ---- S^T = K Q^T: operand reads run kPrefetchK MFMAs ahead ----
-      f32x16 sacc[KT];
-      {
-        auto read_k = [&](int idx) -> bf16x8 {
-          const int t = idx / DS, s = idx % DS;
-          const int key = 32 * t + lo32;
-          const int ch = 2 * s + lh;
-          return bitcast<bf16x8>(sk[key * CPR + (ch ^ swz_k<CPR>(key))]);
-        };
-        bf16x8 ring[kPrefetchK];
-#pragma unroll
-        for (int i = 0; i < kPrefetchK; ++i) ring[i] = read_k(i);
-#pragma unroll
-        for (int idx = 0; idx < KT * DS; ++idx) {
-          const int t = idx / DS, s = idx % DS;
-          const bf16x8 a = ring[idx % kPrefetchK];
-          if (idx + kPrefetchK < KT * DS) ring[idx % kPrefetchK] = read_k(idx + kPrefetchK);
-          sacc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[s], s == 0 ? f32x16{} : sacc[t], 0, 0, 0);
-          constexpr int kDmaEvery = (KT * DS) / (2 * LPW) > 0 ? (KT * DS) / (2 * LPW) : 1;
-          if (has_next && idx % kDmaEvery == kDmaEvery - 1 && idx / kDmaEvery < 2 * LPW)
-            issue_one(nsrc, idx / kDmaEvery, nk, nv);
-          __builtin_amdgcn_sched_barrier(0);   // keep the read-ahead order as written
-        }
-        // (copies that did not fit between the MFMAs, if any)
-        if (has_next) {
-#pragma unroll
-          for (int i = (KT * DS) / ((KT * DS) / (2 * LPW) > 0 ? (KT * DS) / (2 * LPW) : 1); i < 2 * LPW; ++i)
-            issue_one(nsrc, i, nk, nv);
-        }
+    const StageSrc ksrc = stage_src(Kb, c_next, (j + 1) % SPB);
+    const StageSrc vsrc = stage_src(Vb, c, half);
+    // Copy step d of this stage: K_{j+1} first (when there is a next stage), then V_j.
+    auto issue_dma = [&](int d) {
+      if (d < LPW) {
+        if (has_next) issue_one(ksrc, d, true, nk);
+      } else {
+        issue_one(vsrc, d - LPW, false, nv);
       }
+    };
 
-      // ---- mask keys past N (partial stage of the last block) ----
-      if (valid < SUB) {
-        // (opaque bound: keeps the comparisons inside this rarely taken branch)
-        int lv = valid - 4 * lh;
-        asm volatile("" : "+v"(lv));
+    // ---- S^T = K Q^T: operand reads run kPrefetchK MFMAs ahead; the copy of
+    // the next stage is issued in small steps between the MFMAs ----
+    f32x16 sacc[KT];
+    {
+      // K operand of step (t, s): key 32*t + l32, chunk 2*s + h, swizzled
+      // by l32 & (CPR-1); the chunk bits of s enter as an XOR with 32*s.
+      auto read_k = [&](int idx) -> bf16x8 {
+        const int t = idx / DS, s = idx % DS;
+        const char* p = reinterpret_cast<const char*>(sk) + 32 * t * (2 * D) + (k_lane ^ (uint32_t)(32 * s));
+        return bitcast<bf16x8>(*reinterpret_cast<const uint4*>(p));
+      };
+      constexpr int kDmaEvery = (KT * DS) / (2 * LPW) > 0 ? (KT * DS) / (2 * LPW) : 1;
+      bf16x8 ring[kPrefetchK];
 #pragma unroll
-        for (int t = 0; t < KT; ++t)
+      for (int i = 0; i < kPrefetchK; ++i) ring[i] = read_k(i);
 #pragma unroll
-          for (int a = 0; a < 16; ++a) {
-            const int key = 32 * t + 8 * (a >> 2) + (a & 3);
-            if (key >= lv) sacc[t][a] = -INFINITY;
-          }
+      for (int idx = 0; idx < KT * DS; ++idx) {
+        const int t = idx / DS, s = idx % DS;
+        const bf16x8 a = ring[idx % kPrefetchK];
+        if (idx + kPrefetchK < KT * DS) ring[idx % kPrefetchK] = read_k(idx + kPrefetchK);
+        sacc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[s], s == 0 ? f32x16{} : sacc[t], 0, 0, 0);
+        if (idx % kDmaEvery == kDmaEvery - 1 && idx / kDmaEvery < 2 * LPW) issue_dma(idx / kDmaEvery);
+        __builtin_amdgcn_sched_barrier(0);   // keep the read-ahead order as written
       }
-
-      // ---- online softmax (fp32, log2 domain, lazy rescale) ----
-      float mx = -INFINITY;
+      // (copies that did not fit between the MFMAs, if any)
 #pragma unroll
-      for (int t = 0; t < KT; ++t)
-#pragma unroll
-        for (int a = 0; a < 16; ++a) mx = fmaxf(mx, sacc[t][a]);
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
-      const float mb = mx * scale_log2;
-      if (__ballot(mb > m_run + kRescaleThreshold) != 0) {
-        const float m_new = fmaxf(m_run, mb);
-        const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);   // 0 while m_run is -inf
-        m_run = m_new;
-        l_run *= alpha;
-#pragma unroll
-        for (int u = 0; u < DT; ++u)
-#pragma unroll
-          for (int a = 0; a < 16; ++a) oacc[u][a] *= alpha;
-      }
-      // Probabilities go to bf16 in pairs; the row sum adds those same bf16
-      // values (v_dot2 against 1.0), so numerator and denominator of O use
-      // identical weights.
-      const float neg_m = -m_run;
-      const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
-      float psum0 = 0.0f, psum1 = 0.0f;
-      uint32_t pk[KS][4];
-#pragma unroll
-      for (int t = 0; t < KT; ++t)
-#pragma unroll
-        for (int a = 0; a < 16; a += 2) {
-          const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[t][a], scale_log2, neg_m));
-          const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[t][a + 1], scale_log2, neg_m));
-          const bf16x2 two = __builtin_convertvector((f32x2){p0, p1}, bf16x2);
-          if ((a >> 1) & 1) psum1 = __builtin_amdgcn_fdot2_f32_bf16(two, ones, psum1, false);
-          else psum0 = __builtin_amdgcn_fdot2_f32_bf16(two, ones, psum0, false);
-          pk[2 * t + (a >> 3)][(a & 7) >> 1] = bitcast<uint32_t>(two);
-        }
-      l_run += psum0 + psum1;
-
-      // ---- O^T += V^T P^T: transposed reads run kPrefetchV MFMAs ahead ----
-      {
-        auto read_v = [&](int idx) -> bf16x8 {
-          const int sl = idx / DT, u = idx % DT;
-          const int key_lo = 16 * sl + 4 * (g >> 1) + (jj >> 2);
-          const int key_hi = key_lo + 8;
-          const int dcol = 32 * u + 16 * (g & 1) + 4 * (jj & 3);
-          const int ch = dcol >> 3;
-          const int hb = (dcol >> 2) & 1;
-          struct { i16x4 lo, hi; } both;
-          both.lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              (lds_i16x4*)(sv + (key_lo * CPR + (ch ^ swz_v<CPR>(key_lo))) * 16 + hb * 8));
-          both.hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              (lds_i16x4*)(sv + (key_hi * CPR + (ch ^ swz_v<CPR>(key_hi))) * 16 + hb * 8));
-          return bitcast<bf16x8>(both);
-        };
-        bf16x8 ring[kPrefetchV];
-#pragma unroll
-        for (int i = 0; i < kPrefetchV; ++i) ring[i] = read_v(i);
-#pragma unroll
-        for (int idx = 0; idx < KS * DT; ++idx) {
-          const int sl = idx / DT, u = idx % DT;
-          const bf16x8 a = ring[idx % kPrefetchV];
-          if (idx + kPrefetchV < KS * DT) ring[idx % kPrefetchV] = read_v(idx + kPrefetchV);
-          oacc[u] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bitcast<bf16x8>(pk[sl]), oacc[u], 0, 0, 0);
-          __builtin_amdgcn_sched_barrier(0);   // keep the read-ahead order as written
-        }
-      }
-    } else if (has_next) {
-      // fully padded stage: nothing to compute, only the next copy to issue
-#pragma unroll
-      for (int i = 0; i < 2 * LPW; ++i) issue_one(nsrc, i, nk, nv);
+      for (int d = (KT * DS) / kDmaEvery; d < 2 * LPW; ++d) issue_dma(d);
     }
+
+    // ---- mask keys past N (last block only; a stage wholly past N, the
+    // second half of a short last block, is masked entirely) ----
+    const int valid = n_tok - (c * BLK + half * SUB);
+    if (valid < SUB) {
+      // (opaque bound: keeps the comparisons inside this rarely taken branch)
+      int lv = valid - 4 * h;
+      asm volatile("" : "+v"(lv));
+#pragma unroll
+      for (int t = 0; t < KT; ++t)
+#pragma unroll
+        for (int a = 0; a < 16; ++a) {
+          const int key = 32 * t + 8 * (a >> 2) + (a & 3);
+          if (key >= lv) sacc[t][a] = -INFINITY;
+        }
+    }
+
+    // ---- online softmax (fp32, log2 domain, lazy rescale) ----
+    // Each lane holds half of a query's keys. The reference maximum m_run is
+    // shared by both halves and only moves when some lane's own maximum
+    // exceeds it by more than the threshold; only then are the two halves
+    // combined (the common case needs no exchange between lanes). A moved
+    // reference scales O and l by alpha after the pending PV product, whose
+    // terms, like O, are relative to the old reference.
+    float mx = -INFINITY;
+#pragma unroll
+    for (int t = 0; t < KT; ++t)
+#pragma unroll
+      for (int a = 0; a < 16; ++a) mx = fmaxf(mx, sacc[t][a]);
+    const float mb = mx * scale_log2;
+    const bool moved = __ballot(mb > m_run + kRescaleThreshold) != 0;
+    float alpha = 1.0f;
+    if (moved) {
+      const float m_new = fmaxf(m_run, fmaxf(mb, __shfl_xor(mb, 32)));
+      alpha = __builtin_amdgcn_exp2f(m_run - m_new);   // 0 while m_run is -inf
+      m_run = m_new;
+    }
+    // Probabilities go to bf16 in pairs; the row sum adds those same bf16
+    // values (v_dot2 against 1.0), so numerator and denominator of O use
+    // identical weights.
+    const float neg_m = -m_run;
+    const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
+    float psum0 = 0.0f, psum1 = 0.0f;
+    constexpr int NP = KT * 8;          // probability pairs per lane and stage
+    constexpr int NPV = KS * DT;        // PV MFMAs per stage
+    static_assert(NP % NPV == 0, "pairs per PV step");
+    auto exp_pairs = [&](int idx) {     // pairs [idx, idx+1) * NP/NPV
+#pragma unroll
+      for (int q = idx * (NP / NPV); q < (idx + 1) * (NP / NPV); ++q) {
+        const int t = q >> 3, a = 2 * (q & 7);
+        const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[t][a], scale_log2, neg_m));
+        const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[t][a + 1], scale_log2, neg_m));
+        const bf16x2 two = __builtin_convertvector((f32x2){p0, p1}, bf16x2);
+        if ((a >> 1) & 1) psum1 = __builtin_amdgcn_fdot2_f32_bf16(two, ones, psum1, false);
+        else psum0 = __builtin_amdgcn_fdot2_f32_bf16(two, ones, psum0, false);
+        const uint32_t bits = bitcast<uint32_t>(two);
+        pk_cur[2 * t + (a >> 3)][(a & 7) >> 1] = bits;
+        // Anchors: the results are first used after the PV product, and the
+        // compiler would otherwise sink this work below its MFMAs.
+        asm volatile("" :: "v"(bits));
+        asm volatile("" : "+v"(psum0), "+v"(psum1));
+      }
+    };
+    // ---- O^T += V_{j-1}^T P_{j-1}^T, with the exponentials of stage j in between ----
+    pv_product(svp, pk_prev, exp_pairs);
+    if (moved) {
+      l_run *= alpha;
+#pragma unroll
+      for (int u = 0; u < DT; ++u)
+#pragma unroll
+        for (int a = 0; a < 16; ++a) oacc[u][a] *= alpha;
+    }
+    l_run += psum0 + psum1;
     c = c_next;
   };
   for (int j = 0; j < n_stages; j += 2) {
-    stage_body(j, lds_k0, lds_v0, lds_k1, lds_v1);
-    if (j + 1 < n_stages) stage_body(j + 1, lds_k1, lds_v1, lds_k0, lds_v0);
+    stage_body(j, lds_k0, lds_k1, lds_v1, lds_v0, pkB, pkA);
+    if (j + 1 < n_stages) stage_body(j + 1, lds_k1, lds_k0, lds_v0, lds_v1, pkA, pkB);
+  }
+  // The last stage's PV product: V_{n-1} arrives with the copies of the last stage.
+  wait_vmcnt<0>();
+  if (n_stages > 0) {
+    barrier_no_fence();
+    if ((n_stages - 1) & 1) pv_product(lds_v1, pkB, no_step);
+    else pv_product(lds_v0, pkA, no_step);
   }
 
   // ---- epilogue ----
