@@ -23,6 +23,11 @@ Citations name the web page and the section on it:
     ([Notes] Overall Architecture). Encoding read here: CSR, ascending key
     blocks, plus a per-record heaviest-first order of query blocks.
 
+``skiplist.compile_intervals``
+    The same selection in the pages' own encoding, contiguous key-block
+    intervals per query block ([Notes] Key Design 4; Highlights): one
+    half-open [lo, hi) pair per maximal run of kept key blocks.
+
 ``attention.block_sparse_head``
     Retained connections are computed from the current input's Q, K and V and
     unselected ones are skipped ([Notes] Overall Architecture; [Abstract]).

@@ -61,3 +61,54 @@ def skiplist_to_dense(row_ptr: np.ndarray, col_idx: np.ndarray, T: int, L: int, 
     for row in range(T * L * H * nb):
         out[row, col_idx[row_ptr[row]:row_ptr[row + 1]]] = 1
     return out.reshape(T, L, H, nb, nb)
+
+
+def compile_intervals(masks: np.ndarray):
+    """Interval form of the skip list: (iv_ptr int64 [rows+1], iv int32 [n_iv, 2], order int32 [rows]).
+
+    [Notes] Key Design 4 and Highlights: each binary mask becomes a read-only
+    list of contiguous key-block intervals per query block. Reading: one
+    interval per maximal run of kept key blocks, as the half-open pair
+    [lo, hi) (blocks lo .. hi-1 kept, lo-1 and hi not kept or outside the
+    row), runs in ascending order. Maximal runs make the encoding unique.
+    iv_ptr is the running sum of the per-row run counts. order is the same
+    heaviest-first order as the index-list form, by kept-block count.
+
+    Written from the definition of a run: walk each row once, open a run at a
+    kept block whose left neighbour is not kept, close it after a kept block
+    whose right neighbour is not kept.
+    """
+    masks = np.asarray(masks)
+    if masks.ndim != 5 or masks.shape[3] != masks.shape[4]:
+        raise ValueError("masks must be [T, L, H, nb, nb]")
+    T, L, H, nb, _ = masks.shape
+    rows = masks.reshape(T * L * H * nb, nb) != 0
+
+    runs = []
+    iv_ptr = np.zeros(rows.shape[0] + 1, dtype=np.int64)
+    for row in range(rows.shape[0]):
+        keep = rows[row]
+        lo = None
+        for c in range(nb):
+            if keep[c] and (c == 0 or not keep[c - 1]):
+                lo = c
+            if keep[c] and (c == nb - 1 or not keep[c + 1]):
+                runs.append((lo, c + 1))
+        iv_ptr[row + 1] = len(runs)
+    iv = np.array(runs, dtype=np.int32).reshape(-1, 2)
+
+    counts = rows.sum(axis=1)
+    order = np.empty(rows.shape[0], dtype=np.int32)
+    for rec in range(T * L * H):
+        cnt = counts[rec * nb:(rec + 1) * nb]
+        order[rec * nb:(rec + 1) * nb] = sorted(range(nb), key=lambda r: (-int(cnt[r]), r))
+    return iv_ptr, iv, order
+
+
+def intervals_to_dense(iv_ptr: np.ndarray, iv: np.ndarray, T: int, L: int, H: int, nb: int) -> np.ndarray:
+    """Inverse of the interval encoding: rebuild the uint8 [T, L, H, nb, nb] keep mask."""
+    out = np.zeros((T * L * H * nb, nb), dtype=np.uint8)
+    for row in range(T * L * H * nb):
+        for lo, hi in iv[iv_ptr[row]:iv_ptr[row + 1]]:
+            out[row, lo:hi] = 1
+    return out.reshape(T, L, H, nb, nb)
