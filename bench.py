@@ -5,7 +5,9 @@ skip-list compilation of the layer's block masks (calibatt_compile_skiplist)
 followed by the per-head dual-path layer-call (calibatt_layer_dispatch: one
 attention launch covering block-sparse and anchor-row heads, then the anchor
 broadcast). W untimed warmup steps, then K timed steps bracketed by
-torch.cuda.synchronize().
+torch.cuda.synchronize(). The same layer is also timed through the interval
+form of the skip list (calibatt_compile_intervals + calibatt_layer_dispatch_iv),
+reported under "intervals".
 
 Default workload: a Wan-720p-shaped layer (H=40, N=75600 = 21x45x80 tokens,
 d=128, 128x128 blocks, bf16), 32 block-sparse heads at 68% mean sparsity
@@ -197,6 +199,17 @@ def dictionary_sweep(args):
             compile_ms = (time.perf_counter() - t0) * 1e3 / reps
             mask_bytes = masks.size
             out_bytes = 4 * sl.nnz + 8 * (masks.shape[1] * masks.shape[2] * cfg.nb + 1) + 4 * masks.shape[1] * masks.shape[2] * cfg.nb
+            il = cal.compile_intervals(dm, cfg.N, cfg.B)
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            for _ in range(reps):
+                cal.calibatt_compile_intervals(dm, 1, cfg.L, cfg.H, cfg.N, cfg.B, il.iv_ptr, il.iv, il.iv.numel(),
+                                               il.order, stream)
+            torch.cuda.synchronize()
+            compile_iv_ms = (time.perf_counter() - t0) * 1e3 / reps
+            rows = masks.shape[1] * masks.shape[2] * cfg.nb
+            n_iv = il.n_iv
+            del il
             layer_ms, flops = [], 0.0
             for l in range(min(args.sweep_layers, cfg.L)):
                 a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -220,6 +233,9 @@ def dictionary_sweep(args):
                               "block_sparsity": round(1.0 - float(masks.astype(np.float64).mean()), 4),
                               "compile_ms": round(compile_ms, 3),
                               "compile_GBps": round((2 * mask_bytes + out_bytes) / compile_ms / 1e6, 1),
+                              "runs": n_iv, "compile_intervals_ms": round(compile_iv_ms, 3),
+                              "list_MB_index_form": round((8 * (rows + 1) + 4 * sl.nnz) / 1e6, 2),
+                              "list_MB_interval_form": round((8 * (rows + 1) + 4 * n_iv) / 1e6, 2),
                               "layer_ms_mean": round(float(np.mean(layer_ms)), 3),
                               "layer_ms": [round(x, 3) for x in layer_ms],
                               "tflops_mean": round(flops / len(layer_ms), 1)}), flush=True)
@@ -314,6 +330,30 @@ def main():
     torch.cuda.synchronize()
     compile_ms = (time.perf_counter() - t_c) * 1e3 / 5
 
+    # the same layer through the interval form of the skip list
+    il = cal.compile_intervals(masks, cfg.N, cfg.B)
+    t_c = time.perf_counter()
+    for _ in range(5):
+        cal.calibatt_compile_intervals(masks, T, L, H, cfg.N, cfg.B, il.iv_ptr, il.iv, il.iv.numel(), il.order,
+                                       stream)
+    torch.cuda.synchronize()
+    compile_iv_ms = (time.perf_counter() - t_c) * 1e3 / 5
+    cal.calibatt_layer_dispatch_iv(q, k, v, o, lse, il, 0, 0, wl.rep_flags, cfg.F, cfg.R, cfg.C, wl.anchors,
+                                   scale=wl.scale, stream=stream)
+    e0.record(stream)
+    for _ in range(reps):
+        cal.calibatt_layer_dispatch_iv(q, k, v, o, lse, il, 0, 0, wl.rep_flags, cfg.F, cfg.R, cfg.C, wl.anchors,
+                                       scale=wl.scale, stream=stream)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    layer_iv_ms = e0.elapsed_time(e1) / reps
+    rows = T * L * H * nb
+    intervals = {"runs": il.n_iv, "kept_blocks": sl.nnz, "compile_ms": round(compile_iv_ms, 3),
+                 "layer_call_ms": round(layer_iv_ms, 3),
+                 "list_bytes_index_form": 8 * (rows + 1) + 4 * sl.nnz,
+                 "list_bytes_interval_form": 8 * (rows + 1) + 4 * il.n_iv}
+    del il
+
     dense_ms = None
     if not args.no_dense:
         ones = torch.ones((1, 1, H, nb, nb), dtype=torch.uint8, device=dev)
@@ -369,6 +409,7 @@ def main():
         "dense_same_kernel_ms": round(dense_ms, 3) if dense_ms else None,
         "dense_tflops": round(work["flops_dense"] / (dense_ms * 1e-3) / 1e12, 1) if dense_ms else None,
         "speedup_vs_dense": round(dense_ms / layer_ms, 3) if dense_ms else None,
+        "intervals": intervals,
         "sparsity": {"token_sparse_heads": work["token_sparsity_sparse_heads"],
                      "block_sparse_heads": work["block_sparsity_sparse_heads"],
                      "anchor_query": work["anchor_query_sparsity"],

@@ -3,17 +3,22 @@
 The names follow the C ABI in include/calibatt.h:
 
 * ``calibatt_compile_skiplist`` / ``compile_skiplist`` -- block masks -> CSR skip lists on the GPU
-* ``calibatt_block_sparse_attn`` -- block-sparse attention over listed key blocks
+* ``calibatt_compile_intervals`` / ``compile_intervals`` -- block masks -> runs of kept key blocks
+* ``calibatt_block_sparse_attn`` (``_iv``) -- block-sparse attention over listed key blocks
 * ``calibatt_anchor_attn`` -- anchor-row attention plus broadcast
-* ``calibatt_layer_dispatch`` -- one layer-call, per-head choice of path
+* ``calibatt_layer_dispatch`` (``_iv``) -- one layer-call, per-head choice of path
 
 All computation happens in the library's HIP kernels; this package only
 marshals arguments. Importing it fails if the library has not been built.
 """
-from ._lib import (BF16, F32, CalibattError, SkipList, SkipListView, calibatt_anchor_attn,
-                   calibatt_block_sparse_attn, calibatt_compile_skiplist, calibatt_layer_dispatch,
-                   calibatt_set_kernel_events, calibatt_version, compile_skiplist, last_error)
+from ._lib import (BF16, F32, CalibattError, IntervalList, IntervalListView, SkipList, SkipListView,
+                   calibatt_anchor_attn, calibatt_block_sparse_attn, calibatt_block_sparse_attn_iv,
+                   calibatt_compile_intervals, calibatt_compile_skiplist, calibatt_layer_dispatch,
+                   calibatt_layer_dispatch_iv, calibatt_set_kernel_events, calibatt_version,
+                   compile_intervals, compile_skiplist, last_error)
 
-__all__ = ["BF16", "F32", "CalibattError", "SkipList", "SkipListView", "calibatt_anchor_attn",
-           "calibatt_block_sparse_attn", "calibatt_compile_skiplist", "calibatt_layer_dispatch",
-           "calibatt_set_kernel_events", "calibatt_version", "compile_skiplist", "last_error"]
+__all__ = ["BF16", "F32", "CalibattError", "IntervalList", "IntervalListView", "SkipList", "SkipListView",
+           "calibatt_anchor_attn", "calibatt_block_sparse_attn", "calibatt_block_sparse_attn_iv",
+           "calibatt_compile_intervals", "calibatt_compile_skiplist", "calibatt_layer_dispatch",
+           "calibatt_layer_dispatch_iv", "calibatt_set_kernel_events", "calibatt_version",
+           "compile_intervals", "compile_skiplist", "last_error"]

@@ -22,7 +22,8 @@ MAX_HEADS, MAX_ANCHORS, MAX_NB = 256, 64, 4096
 
 EXPORTED = (
     "calibatt_compile_skiplist", "calibatt_block_sparse_attn", "calibatt_anchor_attn",
-    "calibatt_layer_dispatch", "calibatt_last_error", "calibatt_set_kernel_events", "calibatt_version",
+    "calibatt_layer_dispatch", "calibatt_compile_intervals", "calibatt_block_sparse_attn_iv",
+    "calibatt_layer_dispatch_iv", "calibatt_last_error", "calibatt_set_kernel_events", "calibatt_version",
 )
 
 
@@ -37,6 +38,13 @@ class SkipListView(ctypes.Structure):
     _fields_ = [("T", ctypes.c_int32), ("L", ctypes.c_int32), ("H", ctypes.c_int32),
                 ("N", ctypes.c_int32), ("B", ctypes.c_int32), ("nb", ctypes.c_int32),
                 ("row_ptr", ctypes.c_void_p), ("col_idx", ctypes.c_void_p), ("order", ctypes.c_void_p)]
+
+
+class IntervalListView(ctypes.Structure):
+    """Mirror of calibatt_intervals_t."""
+    _fields_ = [("T", ctypes.c_int32), ("L", ctypes.c_int32), ("H", ctypes.c_int32),
+                ("N", ctypes.c_int32), ("B", ctypes.c_int32), ("nb", ctypes.c_int32),
+                ("iv_ptr", ctypes.c_void_p), ("iv", ctypes.c_void_p), ("order", ctypes.c_void_p)]
 
 
 def _load():
@@ -62,6 +70,15 @@ def _load():
                                             ctypes.POINTER(SkipListView), i32, i32, vp,
                                             i32, i32, i32, vp, i32, vp]
     lib.calibatt_layer_dispatch.restype = i32
+    lib.calibatt_compile_intervals.argtypes = lib.calibatt_compile_skiplist.argtypes
+    lib.calibatt_compile_intervals.restype = i32
+    lib.calibatt_block_sparse_attn_iv.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, f32,
+                                                  ctypes.POINTER(IntervalListView), i32, i32, vp, i32, vp]
+    lib.calibatt_block_sparse_attn_iv.restype = i32
+    lib.calibatt_layer_dispatch_iv.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, f32,
+                                               ctypes.POINTER(IntervalListView), i32, i32, vp,
+                                               i32, i32, i32, vp, i32, vp]
+    lib.calibatt_layer_dispatch_iv.restype = i32
     lib.calibatt_last_error.argtypes = []
     lib.calibatt_last_error.restype = ctypes.c_char_p
     lib.calibatt_set_kernel_events.argtypes = [vp, vp]
@@ -162,6 +179,56 @@ def compile_skiplist(masks, N: int, B: int, with_order: bool = True, stream=None
     return SkipList(T, L, H, N, B, nb, row_ptr, col_idx, order, nnz)
 
 
+@dataclass
+class IntervalList:
+    """A compiled dictionary in interval form held in device tensors (iv_ptr, iv, order)."""
+    T: int
+    L: int
+    H: int
+    N: int
+    B: int
+    nb: int
+    iv_ptr: object
+    iv: object
+    order: object
+    n_iv: int
+
+    def view(self) -> IntervalListView:
+        return IntervalListView(self.T, self.L, self.H, self.N, self.B, self.nb,
+                                _ptr(self.iv_ptr), _ptr(self.iv),
+                                _ptr(self.order) if self.order is not None else None)
+
+
+def calibatt_compile_intervals(masks, T, L, H, N, B, iv_ptr, iv, iv_capacity, order, stream=None) -> int:
+    """Raw call: device tensors in, returns the run count (raises on error, CAPACITY included)."""
+    n_iv = ctypes.c_int64(-1)
+    st = lib.calibatt_compile_intervals(_ptr(masks), T, L, H, N, B, _ptr(iv_ptr), _ptr(iv),
+                                        int(iv_capacity), _ptr(order), ctypes.byref(n_iv), _stream(stream))
+    if st == ERR_CAPACITY:
+        raise CalibattError(st, last_error() + f" (n_iv={n_iv.value})")
+    _check(st)
+    return n_iv.value
+
+
+def compile_intervals(masks, N: int, B: int, with_order: bool = True, stream=None) -> IntervalList:
+    """Compile uint8 device masks [T, L, H, nb, nb] into an IntervalList (allocates with torch).
+
+    iv holds the packed runs as int32 tensor storage (bit pattern lo | hi << 16).
+    """
+    import torch
+    T, L, H, nb, nb2 = masks.shape
+    if nb != nb2 or nb != -(-N // B):
+        raise ValueError("masks must be [T, L, H, nb, nb] with nb = ceil(N/B)")
+    dev = masks.device
+    rows = T * L * H * nb
+    iv_ptr = torch.empty(rows + 1, dtype=torch.int64, device=dev)
+    n_iv = calibatt_compile_intervals(masks, T, L, H, N, B, iv_ptr, None, 0, None, stream)
+    iv = torch.empty(max(n_iv, 1), dtype=torch.int32, device=dev)
+    order = torch.empty(rows, dtype=torch.int32, device=dev) if with_order else None
+    calibatt_compile_intervals(masks, T, L, H, N, B, iv_ptr, iv, iv.numel(), order, stream)
+    return IntervalList(T, L, H, N, B, nb, iv_ptr, iv, order, n_iv)
+
+
 def calibatt_block_sparse_attn(q, k, v, o, lse, sl: SkipList, t: int, l: int, heads=None,
                                scale: float | None = None, stream=None) -> None:
     H, N, d = q.shape
@@ -172,6 +239,18 @@ def calibatt_block_sparse_attn(q, k, v, o, lse, sl: SkipList, t: int, l: int, he
                                           _dtype_code(q), scale, ctypes.byref(view), t, l,
                                           harr.ctypes.data if harr is not None else None, nh,
                                           _stream(stream)))
+
+
+def calibatt_block_sparse_attn_iv(q, k, v, o, lse, il: IntervalList, t: int, l: int, heads=None,
+                                  scale: float | None = None, stream=None) -> None:
+    H, N, d = q.shape
+    scale = float(np.float32(1.0 / np.sqrt(d))) if scale is None else scale
+    harr, nh = _host_i32(heads)
+    view = il.view()
+    _check(lib.calibatt_block_sparse_attn_iv(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), H, N, d,
+                                             _dtype_code(q), scale, ctypes.byref(view), t, l,
+                                             harr.ctypes.data if harr is not None else None, nh,
+                                             _stream(stream)))
 
 
 def calibatt_anchor_attn(q, k, v, o, lse, F: int, R: int, C: int, anchor_rows, heads=None,
@@ -197,6 +276,20 @@ def calibatt_layer_dispatch(q, k, v, o, lse, sl: SkipList, t: int, l: int, rep_f
     _check(lib.calibatt_layer_dispatch(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), H, N, d,
                                        _dtype_code(q), scale, ctypes.byref(view), t, l,
                                        flags.ctypes.data, F, R, C, aarr.ctypes.data, ka, _stream(stream)))
+
+
+def calibatt_layer_dispatch_iv(q, k, v, o, lse, il: IntervalList, t: int, l: int, rep_flags, F: int, R: int,
+                               C: int, anchor_rows, scale: float | None = None, stream=None) -> None:
+    H, N, d = q.shape
+    scale = float(np.float32(1.0 / np.sqrt(d))) if scale is None else scale
+    flags = np.ascontiguousarray(np.asarray(rep_flags, dtype=np.uint8))
+    if flags.shape != (il.T, il.L, il.H):
+        raise ValueError("rep_flags must be [T, L, H] of the dictionary")
+    aarr, ka = _host_i32(anchor_rows)
+    view = il.view()
+    _check(lib.calibatt_layer_dispatch_iv(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), H, N, d,
+                                          _dtype_code(q), scale, ctypes.byref(view), t, l,
+                                          flags.ctypes.data, F, R, C, aarr.ctypes.data, ka, _stream(stream)))
 
 
 def calibatt_set_kernel_events(begin, end) -> None:

@@ -3,7 +3,7 @@
 // Every argument is checked here, before anything is enqueued; the kernels
 // assume what these checks establish (sizes, supported d and block sizes,
 // head and anchor ranges). The only synchronisation in the library is the
-// read-back of the kept-block count in calibatt_compile_skiplist.
+// read-back of the entry count in the two compile calls.
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -72,9 +72,31 @@ calibatt_status_t check_heads(const int32_t* heads, int32_t n_heads, int32_t H, 
   return CALIBATT_OK;
 }
 
-calibatt_status_t check_skiplist(const calibatt_skiplist_t* sl, int32_t H, int32_t N, int32_t t, int32_t l) {
+// Either form of a compiled dictionary: index lists (row_ptr, col_idx) or runs
+// (row_ptr = iv_ptr, runs = iv).
+struct ListView {
+  int32_t T, L, H, N, B, nb;
+  const int64_t* row_ptr;
+  const int32_t* col_idx;
+  const uint32_t* runs;
+  const int32_t* order;
+};
+
+calibatt_status_t view_of(const calibatt_skiplist_t* sl, ListView* v) {
   if (!sl) return fail(CALIBATT_ERR_INVALID_ARG, "skip list view is NULL");
   if (!sl->row_ptr || !sl->col_idx) return fail(CALIBATT_ERR_INVALID_ARG, "skip list row_ptr/col_idx are NULL");
+  *v = {sl->T, sl->L, sl->H, sl->N, sl->B, sl->nb, sl->row_ptr, sl->col_idx, nullptr, sl->order};
+  return CALIBATT_OK;
+}
+
+calibatt_status_t view_of(const calibatt_intervals_t* il, ListView* v) {
+  if (!il) return fail(CALIBATT_ERR_INVALID_ARG, "interval list view is NULL");
+  if (!il->iv_ptr || !il->iv) return fail(CALIBATT_ERR_INVALID_ARG, "interval list iv_ptr/iv are NULL");
+  *v = {il->T, il->L, il->H, il->N, il->B, il->nb, il->iv_ptr, nullptr, il->iv, il->order};
+  return CALIBATT_OK;
+}
+
+calibatt_status_t check_skiplist(const ListView* sl, int32_t H, int32_t N, int32_t t, int32_t l) {
   if (sl->H != H || sl->N != N)
     return fail(CALIBATT_ERR_INVALID_ARG, "skip list is for H=%d N=%d, call has H=%d N=%d", sl->H, sl->N, H, N);
   if (sl->B != 64 && sl->B != 128) return fail(CALIBATT_ERR_INVALID_ARG, "block size %d is not supported", sl->B);
@@ -122,10 +144,11 @@ void fill_common(calibatt::AttnParams& p, const void* q, const void* k, const vo
   p.xcd_group = 32;
 }
 
-void fill_sparse(calibatt::AttnParams& p, const calibatt_skiplist_t* sl, int32_t t, int32_t l,
+void fill_sparse(calibatt::AttnParams& p, const ListView* sl, int32_t t, int32_t l,
                  const std::vector<int32_t>& heads) {
   p.row_ptr = sl->row_ptr;
   p.col_idx = sl->col_idx;
+  p.runs = sl->runs;
   p.order = sl->order;
   p.rec_head_rows = sl->nb;
   p.rec_row0 = ((int64_t)t * sl->L + l) * sl->H * sl->nb;
@@ -182,6 +205,87 @@ calibatt_status_t run_broadcast(void* o, float* lse, int32_t N, int32_t d, calib
   return CALIBATT_OK;
 }
 
+// Both compile entry points: count (and scan) per row, read the total back,
+// then fill and order. `runs` selects the interval form.
+calibatt_status_t compile_impl(const uint8_t* masks, int32_t T, int32_t L, int32_t H, int32_t N, int32_t B,
+                               int64_t* ptr, void* out, int64_t capacity, int32_t* order, int64_t* total_out,
+                               bool runs, void* stream) {
+  if (!masks || !ptr || !total_out)
+    return fail(CALIBATT_ERR_INVALID_ARG, "masks, the row pointer array and the count output must be non-NULL");
+  if (T < 1 || L < 1 || H < 1 || N < 1 || B < 1)
+    return fail(CALIBATT_ERR_INVALID_ARG, "T, L, H, N and B must be >= 1");
+  const int64_t nb = ceil_div(N, B);
+  if (nb > CALIBATT_MAX_NB) return fail(CALIBATT_ERR_INVALID_ARG, "nb = %lld exceeds %d", (long long)nb, CALIBATT_MAX_NB);
+  if (out && capacity < 0) return fail(CALIBATT_ERR_INVALID_ARG, "capacity must be >= 0");
+  const int64_t records = (int64_t)T * L * H;
+  const int64_t rows = records * nb;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+
+  hipError_t e = runs ? calibatt::launch_compile_runs_count_scan(masks, rows, (int)nb, ptr, s)
+                      : calibatt::launch_compile_count_scan(masks, rows, (int)nb, ptr, s);
+  if (e != hipSuccess) return hip_fail(e, "skip-list count kernel launch");
+  int64_t total = 0;
+  e = hipMemcpyAsync(&total, ptr + rows, sizeof(int64_t), hipMemcpyDeviceToHost, s);
+  if (e != hipSuccess) return hip_fail(e, "reading the entry count");
+  e = hipStreamSynchronize(s);
+  if (e != hipSuccess) return hip_fail(e, "synchronising after the count pass");
+  *total_out = total;
+  if (!out) return ok();
+  if (capacity < total)
+    return fail(CALIBATT_ERR_CAPACITY, "the output holds %lld entries, %lld needed", (long long)capacity,
+                (long long)total);
+  e = runs ? calibatt::launch_compile_runs_fill(masks, rows, (int)nb, ptr, static_cast<uint32_t*>(out), s)
+           : calibatt::launch_compile_fill(masks, rows, (int)nb, ptr, static_cast<int32_t*>(out), s);
+  if (e != hipSuccess) return hip_fail(e, "skip-list fill kernel launch");
+  if (order) {
+    e = runs ? calibatt::launch_compile_runs_order(ptr, static_cast<const uint32_t*>(out), records, (int)nb, order, s)
+             : calibatt::launch_compile_order(ptr, records, (int)nb, order, s);
+    if (e != hipSuccess) return hip_fail(e, "skip-list order kernel launch");
+  }
+  return ok();
+}
+
+calibatt_status_t sparse_impl(const void* q, const void* k, const void* v, void* o, float* lse, int32_t H,
+                              int32_t N, int32_t d, calibatt_dtype_t dtype, float scale, const ListView* sl,
+                              int32_t t, int32_t l, const int32_t* heads, int32_t n_heads, void* stream) {
+  calibatt_status_t st = check_skiplist(sl, H, N, t, l);
+  if (st != CALIBATT_OK) return st;
+  std::vector<int32_t> hs;
+  if ((st = check_heads(heads, n_heads, H, hs)) != CALIBATT_OK) return st;
+  calibatt::AttnParams p;
+  fill_common(p, q, k, v, o, lse, N, d, sl->B, scale);
+  fill_sparse(p, sl, t, l, hs);
+  if ((st = run_attention(p, d, sl->B, dtype, static_cast<hipStream_t>(stream))) != CALIBATT_OK) return st;
+  return ok();
+}
+
+calibatt_status_t dispatch_impl(const void* q, const void* k, const void* v, void* o, float* lse, int32_t H,
+                                int32_t N, int32_t d, calibatt_dtype_t dtype, float scale, const ListView* sl,
+                                int32_t t, int32_t l, const uint8_t* rep_flags, int32_t F, int32_t R, int32_t C,
+                                const int32_t* anchor_rows, int32_t k_anchors, void* stream) {
+  calibatt_status_t st = check_skiplist(sl, H, N, t, l);
+  if (st != CALIBATT_OK) return st;
+  if (!rep_flags) return fail(CALIBATT_ERR_INVALID_ARG, "rep_flags is NULL");
+  if (H > CALIBATT_MAX_HEADS) return fail(CALIBATT_ERR_INVALID_ARG, "at most %d heads", CALIBATT_MAX_HEADS);
+  // Record selection: the flags of (t, l) split the heads into the two paths.
+  std::vector<int32_t> sparse_heads, rep_heads;
+  const uint8_t* fl = rep_flags + ((int64_t)t * sl->L + l) * sl->H;
+  for (int32_t h = 0; h < H; ++h) (fl[h] ? rep_heads : sparse_heads).push_back(h);
+  if (!rep_heads.empty() && (st = check_anchors(N, F, R, C, anchor_rows, k_anchors)) != CALIBATT_OK) return st;
+  // One launch covers both paths: anchor tiles (every key block) first, then
+  // the block-sparse query blocks.
+  calibatt::AttnParams p;
+  fill_common(p, q, k, v, o, lse, N, d, sl->B, scale);
+  fill_sparse(p, sl, t, l, sparse_heads);
+  if (!rep_heads.empty()) fill_anchor(p, F, R, C, anchor_rows, k_anchors, rep_heads, sl->B);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if ((st = run_attention(p, d, sl->B, dtype, s)) != CALIBATT_OK) return st;
+  if (!rep_heads.empty() &&
+      (st = run_broadcast(o, lse, N, d, dtype, F, R, C, anchor_rows, k_anchors, rep_heads, s)) != CALIBATT_OK)
+    return st;
+  return ok();
+}
+
 }  // namespace
 
 extern "C" {
@@ -198,35 +302,13 @@ void calibatt_set_kernel_events(void* begin, void* end) {
 calibatt_status_t calibatt_compile_skiplist(const uint8_t* masks, int32_t T, int32_t L, int32_t H, int32_t N,
                                             int32_t B, int64_t* row_ptr, int32_t* col_idx, int64_t col_capacity,
                                             int32_t* order, int64_t* nnz_out, void* stream) {
-  if (!masks || !row_ptr || !nnz_out) return fail(CALIBATT_ERR_INVALID_ARG, "masks, row_ptr and nnz_out must be non-NULL");
-  if (T < 1 || L < 1 || H < 1 || N < 1 || B < 1)
-    return fail(CALIBATT_ERR_INVALID_ARG, "T, L, H, N and B must be >= 1");
-  const int64_t nb = ceil_div(N, B);
-  if (nb > CALIBATT_MAX_NB) return fail(CALIBATT_ERR_INVALID_ARG, "nb = %lld exceeds %d", (long long)nb, CALIBATT_MAX_NB);
-  if (col_idx && col_capacity < 0) return fail(CALIBATT_ERR_INVALID_ARG, "col_capacity must be >= 0");
-  const int64_t records = (int64_t)T * L * H;
-  const int64_t rows = records * nb;
-  hipStream_t s = static_cast<hipStream_t>(stream);
+  return compile_impl(masks, T, L, H, N, B, row_ptr, col_idx, col_capacity, order, nnz_out, false, stream);
+}
 
-  hipError_t e = calibatt::launch_compile_count_scan(masks, rows, (int)nb, row_ptr, s);
-  if (e != hipSuccess) return hip_fail(e, "skip-list count kernel launch");
-  int64_t nnz = 0;
-  e = hipMemcpyAsync(&nnz, row_ptr + rows, sizeof(int64_t), hipMemcpyDeviceToHost, s);
-  if (e != hipSuccess) return hip_fail(e, "reading the kept-block count");
-  e = hipStreamSynchronize(s);
-  if (e != hipSuccess) return hip_fail(e, "synchronising after the count pass");
-  *nnz_out = nnz;
-  if (!col_idx) return ok();
-  if (col_capacity < nnz)
-    return fail(CALIBATT_ERR_CAPACITY, "col_idx holds %lld entries, %lld needed", (long long)col_capacity,
-                (long long)nnz);
-  e = calibatt::launch_compile_fill(masks, rows, (int)nb, row_ptr, col_idx, s);
-  if (e != hipSuccess) return hip_fail(e, "skip-list fill kernel launch");
-  if (order) {
-    e = calibatt::launch_compile_order(row_ptr, records, (int)nb, order, s);
-    if (e != hipSuccess) return hip_fail(e, "skip-list order kernel launch");
-  }
-  return ok();
+calibatt_status_t calibatt_compile_intervals(const uint8_t* masks, int32_t T, int32_t L, int32_t H, int32_t N,
+                                             int32_t B, int64_t* iv_ptr, uint32_t* iv, int64_t iv_capacity,
+                                             int32_t* order, int64_t* n_iv_out, void* stream) {
+  return compile_impl(masks, T, L, H, N, B, iv_ptr, iv, iv_capacity, order, n_iv_out, true, stream);
 }
 
 calibatt_status_t calibatt_block_sparse_attn(const void* q, const void* k, const void* v, void* o, float* lse,
@@ -235,14 +317,20 @@ calibatt_status_t calibatt_block_sparse_attn(const void* q, const void* k, const
                                              const int32_t* heads, int32_t n_heads, void* stream) {
   calibatt_status_t st = check_tensors(q, k, v, o, H, N, d, dtype, scale);
   if (st != CALIBATT_OK) return st;
-  if ((st = check_skiplist(sl, H, N, t, l)) != CALIBATT_OK) return st;
-  std::vector<int32_t> hs;
-  if ((st = check_heads(heads, n_heads, H, hs)) != CALIBATT_OK) return st;
-  calibatt::AttnParams p;
-  fill_common(p, q, k, v, o, lse, N, d, sl->B, scale);
-  fill_sparse(p, sl, t, l, hs);
-  if ((st = run_attention(p, d, sl->B, dtype, static_cast<hipStream_t>(stream))) != CALIBATT_OK) return st;
-  return ok();
+  ListView view;
+  if ((st = view_of(sl, &view)) != CALIBATT_OK) return st;
+  return sparse_impl(q, k, v, o, lse, H, N, d, dtype, scale, &view, t, l, heads, n_heads, stream);
+}
+
+calibatt_status_t calibatt_block_sparse_attn_iv(const void* q, const void* k, const void* v, void* o, float* lse,
+                                                int32_t H, int32_t N, int32_t d, calibatt_dtype_t dtype,
+                                                float scale, const calibatt_intervals_t* il, int32_t t, int32_t l,
+                                                const int32_t* heads, int32_t n_heads, void* stream) {
+  calibatt_status_t st = check_tensors(q, k, v, o, H, N, d, dtype, scale);
+  if (st != CALIBATT_OK) return st;
+  ListView view;
+  if ((st = view_of(il, &view)) != CALIBATT_OK) return st;
+  return sparse_impl(q, k, v, o, lse, H, N, d, dtype, scale, &view, t, l, heads, n_heads, stream);
 }
 
 calibatt_status_t calibatt_anchor_attn(const void* q, const void* k, const void* v, void* o, float* lse, int32_t H,
@@ -272,26 +360,23 @@ calibatt_status_t calibatt_layer_dispatch(const void* q, const void* k, const vo
                                           const int32_t* anchor_rows, int32_t k_anchors, void* stream) {
   calibatt_status_t st = check_tensors(q, k, v, o, H, N, d, dtype, scale);
   if (st != CALIBATT_OK) return st;
-  if ((st = check_skiplist(sl, H, N, t, l)) != CALIBATT_OK) return st;
-  if (!rep_flags) return fail(CALIBATT_ERR_INVALID_ARG, "rep_flags is NULL");
-  if (H > CALIBATT_MAX_HEADS) return fail(CALIBATT_ERR_INVALID_ARG, "at most %d heads", CALIBATT_MAX_HEADS);
-  // Record selection: the flags of (t, l) split the heads into the two paths.
-  std::vector<int32_t> sparse_heads, rep_heads;
-  const uint8_t* fl = rep_flags + ((int64_t)t * sl->L + l) * sl->H;
-  for (int32_t h = 0; h < H; ++h) (fl[h] ? rep_heads : sparse_heads).push_back(h);
-  if (!rep_heads.empty() && (st = check_anchors(N, F, R, C, anchor_rows, k_anchors)) != CALIBATT_OK) return st;
-  // One launch covers both paths: anchor tiles (every key block) first, then
-  // the block-sparse query blocks, heaviest first within each head.
-  calibatt::AttnParams p;
-  fill_common(p, q, k, v, o, lse, N, d, sl->B, scale);
-  fill_sparse(p, sl, t, l, sparse_heads);
-  if (!rep_heads.empty()) fill_anchor(p, F, R, C, anchor_rows, k_anchors, rep_heads, sl->B);
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  if ((st = run_attention(p, d, sl->B, dtype, s)) != CALIBATT_OK) return st;
-  if (!rep_heads.empty() &&
-      (st = run_broadcast(o, lse, N, d, dtype, F, R, C, anchor_rows, k_anchors, rep_heads, s)) != CALIBATT_OK)
-    return st;
-  return ok();
+  ListView view;
+  if ((st = view_of(sl, &view)) != CALIBATT_OK) return st;
+  return dispatch_impl(q, k, v, o, lse, H, N, d, dtype, scale, &view, t, l, rep_flags, F, R, C, anchor_rows,
+                       k_anchors, stream);
+}
+
+calibatt_status_t calibatt_layer_dispatch_iv(const void* q, const void* k, const void* v, void* o, float* lse,
+                                             int32_t H, int32_t N, int32_t d, calibatt_dtype_t dtype, float scale,
+                                             const calibatt_intervals_t* il, int32_t t, int32_t l,
+                                             const uint8_t* rep_flags, int32_t F, int32_t R, int32_t C,
+                                             const int32_t* anchor_rows, int32_t k_anchors, void* stream) {
+  calibatt_status_t st = check_tensors(q, k, v, o, H, N, d, dtype, scale);
+  if (st != CALIBATT_OK) return st;
+  ListView view;
+  if ((st = view_of(il, &view)) != CALIBATT_OK) return st;
+  return dispatch_impl(q, k, v, o, lse, H, N, d, dtype, scale, &view, t, l, rep_flags, F, R, C, anchor_rows,
+                       k_anchors, stream);
 }
 
 }  // extern "C"

@@ -88,9 +88,10 @@ __device__ __forceinline__ T bitcast(const S& s) {
 struct Item {
   int head;
   bool anchor;
-  int tile;           // query block (sparse) or anchor tile
-  const int32_t* list;
-  int n;              // number of key blocks to visit
+  int tile;              // query block (sparse) or anchor tile
+  const int32_t* list;   // index-list form: the key blocks
+  const uint32_t* runs;  // interval form: packed runs lo | hi << 16
+  int n;                 // key blocks to visit (index list, anchor), or runs (interval form)
 };
 
 // Logical item of grid block b. Workgroups go round-robin over the 8 XCDs;
@@ -112,6 +113,7 @@ __device__ __forceinline__ Item decode_item(const AttnParams& p, int64_t item) {
     it.head = p.anchor_heads[item / p.anchor_tiles];
     it.tile = (int)(item % p.anchor_tiles);
     it.list = nullptr;
+    it.runs = nullptr;
     it.n = p.nb;
   } else {
     const int64_t j = item - n_anchor_items;
@@ -123,7 +125,8 @@ __device__ __forceinline__ Item decode_item(const AttnParams& p, int64_t item) {
     it.tile = (p.order && p.use_order) ? p.order[rec_row + rank] : rank;
     const int64_t b = p.row_ptr[rec_row + it.tile];
     const int64_t e = p.row_ptr[rec_row + it.tile + 1];
-    it.list = p.col_idx + b;
+    it.list = p.runs ? nullptr : p.col_idx + b;
+    it.runs = p.runs ? p.runs + b : nullptr;
     it.n = (int)(e - b);
   }
   return it;
@@ -180,7 +183,8 @@ void attn_bf16_kernel(const AttnParams p) {
   // buffer of an operand read is an immediate offset; and the item's
   // key-block list.
   __shared__ uint4 lds_kv[4 * STAGE];
-  __shared__ uint16_t lds_list[kListCap];
+  __shared__ uint32_t lds_list32[kListCap / 2];   // index list (as uint16) or runs
+  uint16_t* const lds_list = reinterpret_cast<uint16_t*>(lds_list32);
   uint4* const lds_k0 = lds_kv;
   uint4* const lds_k1 = lds_kv + STAGE;
   uint4* const lds_v0 = lds_kv + 2 * STAGE;
@@ -202,11 +206,14 @@ void attn_bf16_kernel(const AttnParams p) {
   const char* Kb = reinterpret_cast<const char*>(static_cast<const u16*>(p.k) + (int64_t)it.head * p.head_stride);
   const char* Vb = reinterpret_cast<const char*>(static_cast<const u16*>(p.v) + (int64_t)it.head * p.head_stride);
 
-  // The item's key-block list goes to LDS once (n <= nb <= CALIBATT_MAX_NB, as
-  // the host checks), so the loop reads indices with LDS broadcasts instead of
-  // vector-memory loads, which would join the vmcnt queue of the prefetch.
+  // The item's key-block list (or its runs: at most nb/2 of them) goes to LDS
+  // once (nb <= CALIBATT_MAX_NB, as the host checks), so the loop reads
+  // indices with LDS broadcasts instead of vector-memory loads, which would
+  // join the vmcnt queue of the prefetch.
   if (it.list) {
     for (int i = threadIdx.x; i < it.n; i += NW * 64) lds_list[i] = (uint16_t)it.list[i];
+  } else if (it.runs) {
+    for (int i = threadIdx.x; i < it.n; i += NW * 64) lds_list32[i] = it.runs[i];
   }
 
   // Q^T operand fragments: query = wave*32 + l32, d = 16*s + 8*h + [0, 8).
@@ -263,8 +270,25 @@ void attn_bf16_kernel(const AttnParams p) {
   // Lane part of the K operand reads (see read_k).
   const uint32_t k_lane = (uint32_t)(l32 * 2 * D + 16 * (h ^ (l32 & (CPR - 1))));
 
-  // Key block visited at step i (uniform across the workgroup).
-  auto block_at = [&](int i) -> int {
+  // Key blocks in visiting order (uniform across the workgroup). Index lists
+  // and anchor items are indexed by step; runs are walked with a cursor
+  // (current run, its end), advanced once per block.
+  int run_i = 0, run_hi = 0;
+  auto first_block = [&]() -> int {
+    if (it.runs) {
+      const uint32_t w = __builtin_amdgcn_readfirstlane(lds_list32[0]);
+      run_hi = (int)(w >> 16);
+      return (int)(w & 0xffffu);
+    }
+    return it.list ? __builtin_amdgcn_readfirstlane((int)lds_list[0]) : 0;
+  };
+  auto next_block = [&](int c, int i) -> int {   // i: step of the block that follows c
+    if (it.runs) {
+      if (c + 1 < run_hi) return c + 1;
+      const uint32_t w = __builtin_amdgcn_readfirstlane(lds_list32[++run_i]);
+      run_hi = (int)(w >> 16);
+      return (int)(w & 0xffffu);
+    }
     return it.list ? __builtin_amdgcn_readfirstlane((int)lds_list[i]) : i;
   };
 
@@ -289,8 +313,21 @@ void attn_bf16_kernel(const AttnParams p) {
     for (int e = 0; e < 4; ++e) pkB[i][e] = 0u;
   for (int i = threadIdx.x; i < STAGE; i += NW * 64) lds_v1[i] = make_uint4(0, 0, 0, 0);
 
-  const int n_stages = it.n * SPB;
-  int c = n_stages > 0 ? block_at(0) : 0;
+  // Blocks to visit: the run lengths summed (every wave sums the staged runs
+  // itself, so no extra barrier), or the list length.
+  int n_blocks = it.n;
+  if (it.runs) {
+    int part = 0;
+    for (int i = lane; i < it.n; i += 64) {
+      const uint32_t w = lds_list32[i];
+      part += (int)(w >> 16) - (int)(w & 0xffffu);
+    }
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) part += __shfl_xor(part, off);
+    n_blocks = __builtin_amdgcn_readfirstlane(part);
+  }
+  const int n_stages = n_blocks * SPB;
+  int c = n_stages > 0 ? first_block() : 0;
   if (n_stages > 0) {
     const StageSrc src0 = stage_src(Kb, c, 0);
 #pragma unroll
@@ -341,7 +378,7 @@ void attn_bf16_kernel(const AttnParams p) {
                         const uint32_t (&pk_prev)[KS][4], uint32_t (&pk_cur)[KS][4]) {
     const int half = j % SPB;
     const bool has_next = j + 1 < n_stages;
-    const int c_next = (has_next && half == SPB - 1) ? block_at(j / SPB + 1) : c;
+    const int c_next = (has_next && half == SPB - 1) ? next_block(c, j / SPB + 1) : c;
 
     // ---- K_j and V_{j-1} resident in every wave's view; the other buffers are free ----
     wait_vmcnt<0>();

@@ -38,6 +38,7 @@ __global__ __launch_bounds__(BLK) void attn_f32_kernel(const AttnParams p) {
   bool anchor;
   int head, tile, n;
   const int32_t* list;
+  const uint32_t* runs = nullptr;
   if (item < n_anchor_items) {
     anchor = true;
     head = p.anchor_heads[item / p.anchor_tiles];
@@ -52,7 +53,8 @@ __global__ __launch_bounds__(BLK) void attn_f32_kernel(const AttnParams p) {
     const int64_t rec_row = p.rec_row0 + (int64_t)head * p.rec_head_rows;
     tile = (p.order && p.use_order) ? p.order[rec_row + rank] : rank;
     const int64_t b = p.row_ptr[rec_row + tile];
-    list = p.col_idx + b;
+    list = p.runs ? nullptr : p.col_idx + b;
+    runs = p.runs ? p.runs + b : nullptr;
     n = (int)(p.row_ptr[rec_row + tile + 1] - b);
   }
 
@@ -69,31 +71,37 @@ __global__ __launch_bounds__(BLK) void attn_f32_kernel(const AttnParams p) {
   }
   float m = -INFINITY, l = 0.0f;
 
+  // Visit key blocks run by run: a run of the interval form, or one block of
+  // an index list (anchor items: every block).
   for (int step = 0; step < n; ++step) {
-    const int c = list ? list[step] : step;
-    const int nk = min(BLK, p.N - c * BLK);
-    __syncthreads();
-    for (int e = threadIdx.x * 4; e < nk * D; e += BLK * 4) {
-      *reinterpret_cast<float4*>(ks + e) = *reinterpret_cast<const float4*>(K + (int64_t)c * BLK * D + e);
-      *reinterpret_cast<float4*>(vs + e) = *reinterpret_cast<const float4*>(V + (int64_t)c * BLK * D + e);
-    }
-    __syncthreads();
-    for (int j = 0; j < nk; ++j) {
-      float dot = 0.0f;
-#pragma unroll
-      for (int i = 0; i < D; ++i) dot = __builtin_fmaf(q[i], ks[j * D + i], dot);
-      const float s = dot * p.scale;
-      if (s > m) {
-        const float a = expf(m - s);
-        l *= a;
-#pragma unroll
-        for (int i = 0; i < D; ++i) o[i] *= a;
-        m = s;
+    const uint32_t w = runs ? runs[step] : 0u;
+    const int lo = runs ? (int)(w & 0xffffu) : (list ? list[step] : step);
+    const int hi = runs ? (int)(w >> 16) : lo + 1;
+    for (int c = lo; c < hi; ++c) {
+      const int nk = min(BLK, p.N - c * BLK);
+      __syncthreads();
+      for (int e = threadIdx.x * 4; e < nk * D; e += BLK * 4) {
+        *reinterpret_cast<float4*>(ks + e) = *reinterpret_cast<const float4*>(K + (int64_t)c * BLK * D + e);
+        *reinterpret_cast<float4*>(vs + e) = *reinterpret_cast<const float4*>(V + (int64_t)c * BLK * D + e);
       }
-      const float pj = expf(s - m);
-      l += pj;
+      __syncthreads();
+      for (int j = 0; j < nk; ++j) {
+        float dot = 0.0f;
 #pragma unroll
-      for (int i = 0; i < D; ++i) o[i] = __builtin_fmaf(pj, vs[j * D + i], o[i]);
+        for (int i = 0; i < D; ++i) dot = __builtin_fmaf(q[i], ks[j * D + i], dot);
+        const float s = dot * p.scale;
+        if (s > m) {
+          const float a = expf(m - s);
+          l *= a;
+#pragma unroll
+          for (int i = 0; i < D; ++i) o[i] *= a;
+          m = s;
+        }
+        const float pj = expf(s - m);
+        l += pj;
+#pragma unroll
+        for (int i = 0; i < D; ++i) o[i] = __builtin_fmaf(pj, vs[j * D + i], o[i]);
+      }
     }
   }
 

@@ -36,6 +36,8 @@ struct AttnParams {
   const int64_t* row_ptr;
   const int32_t* col_idx;
   const int32_t* order;
+  const uint32_t* runs;     // interval form: packed runs lo | hi << 16 (row_ptr then
+                            // offsets runs, col_idx is unused); NULL for index lists
   int64_t rec_row0;         // skip-list row of (t, l, head 0, block 0)
   int32_t rec_head_rows;    // rows per record (= nb)
   int32_t n_sparse;
@@ -78,5 +80,11 @@ hipError_t launch_compile_fill(const uint8_t* masks, int64_t rows, int nb, const
                                int32_t* col_idx, hipStream_t s);
 hipError_t launch_compile_order(const int64_t* row_ptr, int64_t records, int nb, int32_t* order,
                                 hipStream_t s);
+hipError_t launch_compile_runs_count_scan(const uint8_t* masks, int64_t rows, int nb, int64_t* iv_ptr,
+                                          hipStream_t s);
+hipError_t launch_compile_runs_fill(const uint8_t* masks, int64_t rows, int nb, const int64_t* iv_ptr,
+                                    uint32_t* iv, hipStream_t s);
+hipError_t launch_compile_runs_order(const int64_t* iv_ptr, const uint32_t* iv, int64_t records, int nb,
+                                     int32_t* order, hipStream_t s);
 
 }  // namespace calibatt

@@ -94,8 +94,8 @@ typedef struct {
  *   order     int32 [T*L*H*nb], device, written; may be NULL.
  *   nnz_out   host; receives the number of kept blocks (always, when OK or CAPACITY).
  * Returns CALIBATT_ERR_CAPACITY when col_capacity < nnz (col_idx and order are
- * then not written). This is the only call that synchronises `stream` (to
- * read nnz back); it runs offline, before generation.
+ * then not written). The two compile calls are the only ones that synchronise
+ * `stream` (to read the count back); they run offline, before generation.
  */
 calibatt_status_t calibatt_compile_skiplist(const uint8_t* masks, int32_t T, int32_t L, int32_t H,
                                             int32_t N, int32_t B, int64_t* row_ptr, int32_t* col_idx,
@@ -159,13 +159,71 @@ calibatt_status_t calibatt_layer_dispatch(const void* q, const void* k, const vo
                                           const uint8_t* rep_flags, int32_t F, int32_t R, int32_t C,
                                           const int32_t* anchor_rows, int32_t k_anchors, void* stream);
 
+/*
+ * The interval form of a compiled dictionary: the notes' own encoding, a
+ * read-only list of contiguous key-block intervals per query block ([Notes]
+ * Key Design 4; Highlights). One entry per maximal run of kept key blocks,
+ * packed into 32 bits as two 16-bit halves (nb <= CALIBATT_MAX_NB < 2^16):
+ * lo | hi << 16 names blocks lo .. hi-1, all kept; block lo-1 and block hi
+ * are not kept (or lie outside the row). Runs of a row are ascending. A view
+ * of caller-owned device arrays, as produced by calibatt_compile_intervals.
+ *   T, L, H, N, B, nb: as in calibatt_skiplist_t.
+ *   iv_ptr : int64 [T*L*H*nb + 1]; row id*nb + r owns runs iv_ptr[row] .. iv_ptr[row+1]-1.
+ *   iv     : uint32 [iv_ptr[T*L*H*nb]] packed runs.
+ *   order  : int32 [T*L*H*nb] or NULL; the same heaviest-first order as the
+ *            index-list form (by kept-block count).
+ */
+typedef struct {
+  int32_t T, L, H, N, B, nb;
+  const int64_t* iv_ptr;
+  const uint32_t* iv;
+  const int32_t* order;
+} calibatt_intervals_t;
+
+/*
+ * Compile binary block masks into the interval form (same masks, T, L, H, N,
+ * B, order, stream and error rules as calibatt_compile_skiplist).
+ *   iv_ptr    int64 [T*L*H*nb + 1], device, written (iv_ptr[0] = 0).
+ *   iv        uint32 [iv_capacity], device, written; NULL to query the size only.
+ *   n_iv_out  host; receives the number of runs (always, when OK or CAPACITY).
+ * Returns CALIBATT_ERR_CAPACITY when iv_capacity < runs (iv and order are then
+ * not written). Synchronises `stream` once to read the run count back.
+ */
+calibatt_status_t calibatt_compile_intervals(const uint8_t* masks, int32_t T, int32_t L, int32_t H,
+                                             int32_t N, int32_t B, int64_t* iv_ptr, uint32_t* iv,
+                                             int64_t iv_capacity, int32_t* order, int64_t* n_iv_out,
+                                             void* stream);
+
+/*
+ * calibatt_block_sparse_attn over a dictionary in interval form: the kernels
+ * walk each query block's runs directly. Same arguments, rules and results as
+ * calibatt_block_sparse_attn (the key blocks, their order and the arithmetic
+ * are the same, so the outputs are bitwise equal), with `il` in place of `sl`.
+ */
+calibatt_status_t calibatt_block_sparse_attn_iv(const void* q, const void* k, const void* v, void* o,
+                                                float* lse, int32_t H, int32_t N, int32_t d,
+                                                calibatt_dtype_t dtype, float scale,
+                                                const calibatt_intervals_t* il, int32_t t, int32_t l,
+                                                const int32_t* heads, int32_t n_heads, void* stream);
+
+/*
+ * calibatt_layer_dispatch over a dictionary in interval form (rep_flags is
+ * [T][L][H] with T, L, H taken from *il). Bitwise equal to the index-list call.
+ */
+calibatt_status_t calibatt_layer_dispatch_iv(const void* q, const void* k, const void* v, void* o,
+                                             float* lse, int32_t H, int32_t N, int32_t d,
+                                             calibatt_dtype_t dtype, float scale,
+                                             const calibatt_intervals_t* il, int32_t t, int32_t l,
+                                             const uint8_t* rep_flags, int32_t F, int32_t R, int32_t C,
+                                             const int32_t* anchor_rows, int32_t k_anchors, void* stream);
+
 /* Message for the last non-OK status returned on this thread ("" if none). */
 const char* calibatt_last_error(void);
 
 /*
  * Timing hook for benchmarks: the next attention launch made on this thread
- * by calibatt_block_sparse_attn, calibatt_anchor_attn or
- * calibatt_layer_dispatch records hipEvent_t `begin` right before the
+ * by calibatt_block_sparse_attn(_iv), calibatt_anchor_attn or
+ * calibatt_layer_dispatch(_iv) records hipEvent_t `begin` right before the
  * attention kernel and `end` right after it, on the same stream; the hook
  * then clears itself. Pass NULL, NULL to clear it explicitly.
  */

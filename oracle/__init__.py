@@ -61,9 +61,9 @@ Readings of points the pages leave open are listed in the module docstrings
 where they are applied (empty rows, partial last block, anchor ties, token
 order, broadcast unit).
 """
-from .skiplist import compile_skiplist, skiplist_to_dense
+from .skiplist import compile_intervals, compile_skiplist, intervals_to_dense, skiplist_to_dense
 from .attention import (block_sparse_head, anchor_head, nearest_anchor_rows,
                         layer_forward, block_tokens)
 
-__all__ = ["compile_skiplist", "skiplist_to_dense", "block_sparse_head", "anchor_head",
+__all__ = ["compile_intervals", "compile_skiplist", "intervals_to_dense", "skiplist_to_dense", "block_sparse_head", "anchor_head",
            "nearest_anchor_rows", "layer_forward", "block_tokens"]

@@ -120,6 +120,49 @@ def test_compile_rejects():
     assert lib.calibatt_compile_skiplist(P, 1, 1, 1, 100, 10, P, None, 0, None, None, None) == INVALID
 
 
+def _iv_view(T=1, L=1, H=2, N=1000, B=128, nb=8, iv_ptr=P, iv=P):
+    return cal.IntervalListView(T, L, H, N, B, nb, iv_ptr, iv, None)
+
+
+@pytest.mark.parametrize("view,msg", [
+    (None, "NULL"),
+    (_iv_view(iv=None), "iv_ptr/iv"),
+    (_iv_view(iv_ptr=None), "iv_ptr/iv"),
+    (_iv_view(H=3), "skip list is for"),
+    (_iv_view(B=96, nb=11), "block size"),
+    (_iv_view(nb=7), "nb"),
+    (_iv_view(T=0), "T and L"),
+])
+def test_interval_attention_rejects(view, msg):
+    ref = ctypes.byref(view) if view is not None else None
+    st = lib.calibatt_block_sparse_attn_iv(P, P, P, P, None, 2, 1000, 128, cal.BF16, 0.088, ref, 0, 0,
+                                           None, 0, None)
+    assert st == INVALID and msg in cal.last_error()
+    flags = np.zeros((max(view.T, 1) if view else 1, 1, 2), dtype=np.uint8) if view else None
+    st = lib.calibatt_layer_dispatch_iv(P, P, P, P, None, 2, 1000, 128, cal.BF16, 0.088, ref, 0, 0,
+                                        flags.ctypes.data if flags is not None else None, 10, 10, 10, None, 0,
+                                        None)
+    assert st == INVALID and msg in cal.last_error()
+
+
+def test_interval_dispatch_rejects_missing_flags():
+    view = _iv_view()
+    st = lib.calibatt_layer_dispatch_iv(P, P, P, P, None, 2, 1000, 128, cal.BF16, 0.088, ctypes.byref(view), 0,
+                                        0, None, 10, 10, 10, None, 0, None)
+    assert st == INVALID and "rep_flags" in cal.last_error()
+
+
+def test_compile_intervals_rejects():
+    n = ctypes.c_int64(-1)
+    f = lib.calibatt_compile_intervals
+    assert f(None, 1, 1, 1, 100, 10, P, None, 0, None, ctypes.byref(n), None) == INVALID
+    assert f(P, 0, 1, 1, 100, 10, P, None, 0, None, ctypes.byref(n), None) == INVALID
+    assert f(P, 1, 1, 1, 10**6, 1, P, None, 0, None, ctypes.byref(n), None) == INVALID
+    assert "exceeds" in cal.last_error()
+    assert f(P, 1, 1, 1, 100, 10, P, P, -1, None, ctypes.byref(n), None) == INVALID
+    assert f(P, 1, 1, 1, 100, 10, None, None, 0, None, ctypes.byref(n), None) == INVALID
+
+
 def test_product_path_does_not_import_the_oracle():
     import sys
     pkg = os.path.join(ROOT, "calibrated_block_sparse_skiplist_amd")
