@@ -57,6 +57,13 @@ There are no printed attention values on the pages, so beyond these pins the
 attention outputs have no external worked example; no function here is
 "parity unpinned".
 
+``calibration.block_energy`` / ``select_blocks`` / ``keep_counts`` / ``keep_frequency_mask``
+    The offline calibration that produces the masks: block energies of the
+    post-softmax attention (Eq. 5, [Notes] Key Design 1), the shortest
+    descending prefix reaching the energy threshold per query block (same
+    section), and the cross-prompt keep frequency thresholded at rho
+    (Eq. 8-9, [Notes] Key Design 2; A Worked Example).
+
 Readings of points the pages leave open are listed in the module docstrings
 where they are applied (empty rows, partial last block, anchor ties, token
 order, broadcast unit).
@@ -64,6 +71,8 @@ order, broadcast unit).
 from .skiplist import compile_intervals, compile_skiplist, intervals_to_dense, skiplist_to_dense
 from .attention import (block_sparse_head, anchor_head, nearest_anchor_rows,
                         layer_forward, block_tokens)
+from .calibration import block_energy, keep_counts, keep_frequency_mask, select_blocks
 
 __all__ = ["compile_intervals", "compile_skiplist", "intervals_to_dense", "skiplist_to_dense", "block_sparse_head", "anchor_head",
-           "nearest_anchor_rows", "layer_forward", "block_tokens"]
+           "nearest_anchor_rows", "layer_forward", "block_tokens", "block_energy", "keep_counts",
+           "keep_frequency_mask", "select_blocks"]
