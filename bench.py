@@ -55,6 +55,10 @@ def parse_args():
                     help="480p 40x40 dictionary: compile time and per-layer time over sparsity x "
                          "repetitive fraction (one JSON line per point)")
     ap.add_argument("--sweep-layers", type=int, default=4, help="layers timed per sweep point")
+    ap.add_argument("--calibration", action="store_true",
+                    help="offline calibration at the Wan-720p shape: block energies of one prompt (all 40 heads), "
+                         "top-tau selection, keep frequency (one JSON line)")
+    ap.add_argument("--prompts", type=int, default=3, help="calibration prompts timed")
     return ap.parse_args()
 
 
@@ -242,6 +246,64 @@ def dictionary_sweep(args):
             del dm, sl
 
 
+def calibration_bench(args):
+    """Offline calibration of one layer at the Wan-720p shape: per prompt, block energies of all 40 heads
+    (calibatt_block_energy) and their top-tau selection accumulated into keep counts
+    (calibatt_select_blocks); then the keep-frequency mask (calibatt_keep_frequency)."""
+    import torch
+    import workloads
+    import calibrated_block_sparse_skiplist_amd as cal
+    cfg = workloads.get_config("wan720")
+    H, N, d, B, nb = cfg.H, cfg.N, cfg.d, cfg.B, cfg.nb
+    tau, rho = 0.9, 0.5
+    dev = torch.device("cuda")
+    stream = torch.cuda.current_stream()
+    # one prompt's synthetic Q, K in HBM (the timed work does not depend on the values)
+    q, k = workloads.make_calibration_prompts(N, d, cfg.F, cfg.R, cfg.C, H, 1, seed=8000)
+    qd = torch.from_numpy(q[0].view(np.int16)).view(torch.bfloat16).to(dev)
+    kd = torch.from_numpy(k[0].view(np.int16)).view(torch.bfloat16).to(dev)
+    del q, k
+    energy = torch.empty((H, nb, nb), dtype=torch.float32, device=dev)
+    counts = torch.zeros((H, nb, nb), dtype=torch.int32, device=dev)
+    mask = torch.empty((H, nb, nb), dtype=torch.uint8, device=dev)
+    cal.calibatt_block_energy(qd, kd, energy, B, stream=stream)
+    torch.cuda.synchronize()
+    e_ms, s_ms = [], []
+    for _ in range(args.prompts):
+        a, b, c = (torch.cuda.Event(enable_timing=True) for _ in range(3))
+        a.record(stream)
+        b.record(stream)
+        cal.calibatt_set_kernel_events(a.cuda_event, b.cuda_event)
+        cal.calibatt_block_energy(qd, kd, energy, B, stream=stream)
+        cal.calibatt_select_blocks(energy, tau, counts=counts, stream=stream)
+        c.record(stream)
+        torch.cuda.synchronize()
+        e_ms.append(a.elapsed_time(b))
+        s_ms.append(b.elapsed_time(c))
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record(stream)
+    cal.calibatt_keep_frequency(counts, args.prompts, rho, mask, stream=stream)
+    b.record(stream)
+    torch.cuda.synchronize()
+    keep_ms = a.elapsed_time(b)
+    energy_ms = float(np.mean(e_ms))
+    qk_flop = 2.0 * d * N * N * H                  # one QK^T product over all heads
+    executed = 2 * qk_flop                         # the kernel computes the scores twice
+    row_sums = energy.sum(dim=2)
+    print(json.dumps({
+        "mode": "calibration", "workload": "wan720 shape: H=40, N=75600, d=128, 128x128 blocks, bf16",
+        "prompts": args.prompts, "tau": tau, "rho": rho,
+        "energy_ms_per_prompt": round(energy_ms, 3),
+        "energy_tflops_executed": round(executed / (energy_ms * 1e-3) / 1e12, 1),
+        "energy_tflops_algorithmic": round(qk_flop / (energy_ms * 1e-3) / 1e12, 1),
+        "energy_frac_of_bf16_peak_executed": round(executed / (energy_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+        "select_ms_per_prompt": round(float(np.mean(s_ms)), 3),
+        "select_rows": H * nb, "nb": nb, "keep_frequency_ms": round(keep_ms, 3),
+        "kept_fraction_final_mask": round(float(mask.float().mean().item()), 4),
+        "energy_row_sum_max_dev": float((row_sums - 1.0).abs().max().item()),
+    }), flush=True)
+
+
 def main():
     args = parse_args()
     if args.gpus != 1:
@@ -251,6 +313,9 @@ def main():
     import torch
     if args.dictionary_sweep:
         dictionary_sweep(args)
+        return
+    if args.calibration:
+        calibration_bench(args)
         return
     if args.copy_calib:
         src = torch.empty(1 << 28, dtype=torch.float32, device="cuda")

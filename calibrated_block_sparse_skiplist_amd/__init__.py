@@ -7,18 +7,22 @@ The names follow the C ABI in include/calibatt.h:
 * ``calibatt_block_sparse_attn`` (``_iv``) -- block-sparse attention over listed key blocks
 * ``calibatt_anchor_attn`` -- anchor-row attention plus broadcast
 * ``calibatt_layer_dispatch`` (``_iv``) -- one layer-call, per-head choice of path
+* ``calibatt_block_energy`` / ``calibatt_select_blocks`` / ``calibatt_keep_frequency`` -- offline
+  calibration: block energies of a prompt, its top-tau selection, cross-prompt keep frequency
 
 All computation happens in the library's HIP kernels; this package only
 marshals arguments. Importing it fails if the library has not been built.
 """
 from ._lib import (BF16, F32, CalibattError, IntervalList, IntervalListView, SkipList, SkipListView,
-                   calibatt_anchor_attn, calibatt_block_sparse_attn, calibatt_block_sparse_attn_iv,
+                   calibatt_anchor_attn, calibatt_block_energy, calibatt_block_sparse_attn,
+                   calibatt_block_sparse_attn_iv, calibatt_keep_frequency, calibatt_select_blocks,
                    calibatt_compile_intervals, calibatt_compile_skiplist, calibatt_layer_dispatch,
                    calibatt_layer_dispatch_iv, calibatt_set_kernel_events, calibatt_version,
                    compile_intervals, compile_skiplist, last_error)
 
 __all__ = ["BF16", "F32", "CalibattError", "IntervalList", "IntervalListView", "SkipList", "SkipListView",
-           "calibatt_anchor_attn", "calibatt_block_sparse_attn", "calibatt_block_sparse_attn_iv",
+           "calibatt_anchor_attn", "calibatt_block_energy", "calibatt_block_sparse_attn",
+           "calibatt_block_sparse_attn_iv", "calibatt_keep_frequency", "calibatt_select_blocks",
            "calibatt_compile_intervals", "calibatt_compile_skiplist", "calibatt_layer_dispatch",
            "calibatt_layer_dispatch_iv", "calibatt_set_kernel_events", "calibatt_version",
            "compile_intervals", "compile_skiplist", "last_error"]

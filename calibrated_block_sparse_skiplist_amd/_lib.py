@@ -23,7 +23,8 @@ MAX_HEADS, MAX_ANCHORS, MAX_NB = 256, 64, 4096
 EXPORTED = (
     "calibatt_compile_skiplist", "calibatt_block_sparse_attn", "calibatt_anchor_attn",
     "calibatt_layer_dispatch", "calibatt_compile_intervals", "calibatt_block_sparse_attn_iv",
-    "calibatt_layer_dispatch_iv", "calibatt_last_error", "calibatt_set_kernel_events", "calibatt_version",
+    "calibatt_layer_dispatch_iv", "calibatt_block_energy", "calibatt_select_blocks", "calibatt_keep_frequency",
+    "calibatt_last_error", "calibatt_set_kernel_events", "calibatt_version",
 )
 
 
@@ -79,6 +80,12 @@ def _load():
                                                ctypes.POINTER(IntervalListView), i32, i32, vp,
                                                i32, i32, i32, vp, i32, vp]
     lib.calibatt_layer_dispatch_iv.restype = i32
+    lib.calibatt_block_energy.argtypes = [vp, vp, i32, i32, i32, i32, f32, i32, vp, vp, i32, vp]
+    lib.calibatt_block_energy.restype = i32
+    lib.calibatt_select_blocks.argtypes = [vp, i64, i32, f32, vp, vp, vp]
+    lib.calibatt_select_blocks.restype = i32
+    lib.calibatt_keep_frequency.argtypes = [vp, i64, i32, f32, vp, vp]
+    lib.calibatt_keep_frequency.restype = i32
     lib.calibatt_last_error.argtypes = []
     lib.calibatt_last_error.restype = ctypes.c_char_p
     lib.calibatt_set_kernel_events.argtypes = [vp, vp]
@@ -290,6 +297,29 @@ def calibatt_layer_dispatch_iv(q, k, v, o, lse, il: IntervalList, t: int, l: int
     _check(lib.calibatt_layer_dispatch_iv(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), H, N, d,
                                           _dtype_code(q), scale, ctypes.byref(view), t, l,
                                           flags.ctypes.data, F, R, C, aarr.ctypes.data, ka, _stream(stream)))
+
+
+def calibatt_block_energy(q, k, energy, B: int, heads=None, scale: float | None = None, stream=None) -> None:
+    """Block energies [H, nb, nb] (float32 device tensor) of one prompt's q, k [H, N, d]."""
+    H, N, d = q.shape
+    scale = float(np.float32(1.0 / np.sqrt(d))) if scale is None else scale
+    harr, nh = _host_i32(heads)
+    _check(lib.calibatt_block_energy(_ptr(q), _ptr(k), H, N, d, _dtype_code(q), scale, B, _ptr(energy),
+                                     harr.ctypes.data if harr is not None else None, nh, _stream(stream)))
+
+
+def calibatt_select_blocks(energy, tau: float, mask=None, counts=None, stream=None) -> None:
+    """Top-tau selection over the last axis of a float32 energy tensor; writes mask and/or adds to counts."""
+    nb = energy.shape[-1]
+    rows = energy.numel() // nb
+    _check(lib.calibatt_select_blocks(_ptr(energy), rows, nb, float(tau), _ptr(mask), _ptr(counts),
+                                      _stream(stream)))
+
+
+def calibatt_keep_frequency(counts, n_prompts: int, rho: float, mask, stream=None) -> None:
+    """mask = counts / n_prompts >= rho (elementwise, exact)."""
+    _check(lib.calibatt_keep_frequency(_ptr(counts), counts.numel(), n_prompts, float(rho), _ptr(mask),
+                                       _stream(stream)))
 
 
 def calibatt_set_kernel_events(begin, end) -> None:

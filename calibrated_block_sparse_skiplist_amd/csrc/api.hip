@@ -379,4 +379,65 @@ calibatt_status_t calibatt_layer_dispatch_iv(const void* q, const void* k, const
                        k_anchors, stream);
 }
 
+calibatt_status_t calibatt_block_energy(const void* q, const void* k, int32_t H, int32_t N, int32_t d,
+                                        calibatt_dtype_t dtype, float scale, int32_t B, float* energy,
+                                        const int32_t* heads, int32_t n_heads, void* stream) {
+  // (v and o are not used: the placeholders pass the shared tensor checks)
+  calibatt_status_t st = check_tensors(q, k, q, energy, H, N, d, dtype, scale);
+  if (st != CALIBATT_OK) return st;
+  if (B != 64 && B != 128) return fail(CALIBATT_ERR_INVALID_ARG, "block size %d is not supported", B);
+  const int64_t nb = ceil_div(N, B);
+  if (nb > CALIBATT_MAX_NB) return fail(CALIBATT_ERR_INVALID_ARG, "nb exceeds %d", CALIBATT_MAX_NB);
+  std::vector<int32_t> hs;
+  if ((st = check_heads(heads, n_heads, H, hs)) != CALIBATT_OK) return st;
+  calibatt::EnergyParams p;
+  std::memset(&p, 0, sizeof(p));
+  p.q = q;
+  p.k = k;
+  p.energy = energy;
+  p.head_stride = (int64_t)N * d;
+  p.N = N;
+  p.nb = (int32_t)nb;
+  p.scale = scale;
+  p.scale_log2 = scale * 1.4426950408889634f;
+  p.dtype_f32 = dtype == CALIBATT_F32 ? 1 : 0;
+  p.n_heads = (int32_t)hs.size();
+  for (size_t i = 0; i < hs.size(); ++i) p.heads[i] = hs[i];
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipEvent_t eb = g_ev_begin, ee = g_ev_end;
+  g_ev_begin = g_ev_end = nullptr;
+  hipError_t e;
+  if (eb && (e = hipEventRecord(eb, s)) != hipSuccess) return hip_fail(e, "hipEventRecord");
+  if ((e = calibatt::launch_energy(p, d, B, s)) != hipSuccess) return hip_fail(e, "block energy kernel launch");
+  if (ee && (e = hipEventRecord(ee, s)) != hipSuccess) return hip_fail(e, "hipEventRecord");
+  return ok();
+}
+
+calibatt_status_t calibatt_select_blocks(const float* energy, int64_t rows, int32_t nb, float tau, uint8_t* mask,
+                                         int32_t* counts, void* stream) {
+  if (!energy) return fail(CALIBATT_ERR_INVALID_ARG, "energy is NULL");
+  if (!mask && !counts) return fail(CALIBATT_ERR_INVALID_ARG, "mask and counts are both NULL");
+  if (rows < 0) return fail(CALIBATT_ERR_INVALID_ARG, "rows must be >= 0");
+  if (nb < 1 || nb > CALIBATT_MAX_NB) return fail(CALIBATT_ERR_INVALID_ARG, "nb must be in [1, %d]", CALIBATT_MAX_NB);
+  if (!std::isfinite(tau) || tau < 0.0f || tau > 1.0f) return fail(CALIBATT_ERR_INVALID_ARG, "tau must be in [0, 1]");
+  // threshold in 2^-48 units, exact: tau * 2^48 is exact in double
+  const unsigned long long need = (unsigned long long)std::ceil((double)tau * 281474976710656.0);
+  hipError_t e = calibatt::launch_select(energy, rows, nb, need, mask, counts, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "selection kernel launch");
+  return ok();
+}
+
+calibatt_status_t calibatt_keep_frequency(const int32_t* counts, int64_t n, int32_t n_prompts, float rho,
+                                          uint8_t* mask, void* stream) {
+  if (!counts || !mask) return fail(CALIBATT_ERR_INVALID_ARG, "counts and mask must be non-NULL");
+  if (n < 0) return fail(CALIBATT_ERR_INVALID_ARG, "n must be >= 0");
+  if (n_prompts < 1) return fail(CALIBATT_ERR_INVALID_ARG, "n_prompts must be >= 1");
+  if (!std::isfinite(rho) || rho < 0.0f || rho > 1.0f) return fail(CALIBATT_ERR_INVALID_ARG, "rho must be in [0, 1]");
+  // count / |D| >= rho  <=>  count >= rho * |D| (exact product in double)  <=>  count >= ceil(rho * |D|)
+  const int32_t k_min = (int32_t)std::ceil((double)rho * (double)n_prompts);
+  hipError_t e = calibatt::launch_keep(counts, n, k_min, mask, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "keep-frequency kernel launch");
+  return ok();
+}
+
 }  // extern "C"

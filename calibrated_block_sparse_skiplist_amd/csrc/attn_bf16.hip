@@ -33,57 +33,18 @@
 // LDS rows are XOR-swizzled in 16-byte chunks: K by (row & 15), so the 16
 // rows of an MFMA operand read hit distinct banks; V by 4*(row & 3), so the
 // 8-row x 64-byte patch of a transposed read spreads over all banks.
-#include "internal.h"
+#include "gfx950_device.h"
 
 namespace calibatt {
 namespace {
 
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-typedef float f32x2 __attribute__((ext_vector_type(2)));
-typedef short i16x4 __attribute__((ext_vector_type(4)));
-typedef float f32x16 __attribute__((ext_vector_type(16)));
-typedef unsigned short u16;
-typedef __attribute__((address_space(3))) void lds_void;
-typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+using namespace dev;
 
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kRescaleThreshold = 8.0f;   // log2 units: stale maxima are allowed 2^8 headroom
 constexpr int kPrefetchK = 4;               // K operand reads in flight ahead of their MFMA
 constexpr int kPrefetchV = 3;               // V operand reads (2 instructions each) in flight
 constexpr int kListCap = CALIBATT_MAX_NB;   // key-block indices staged in LDS per item (all of them)
-
-template <int CPR>
-__device__ __forceinline__ int swz_k(int row) { return row & (CPR - 1); }
-template <int CPR>
-__device__ __forceinline__ int swz_v(int row) { return (4 * (row & 3)) & (CPR - 1); }
-
-// s_waitcnt with only the vector-memory counter constrained (gfx9 encoding).
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
-}
-
-// Workgroup barrier without a memory fence. __syncthreads() fences, and a
-// workgroup fence must drain every outstanding vector-memory operation,
-// including the LDS DMA prefetch of the next tile; here each wave instead
-// waits for its own DMA with wait_vmcnt before the barrier, and its LDS reads
-// have returned (lgkmcnt 0). The memory clobber keeps LDS accesses on their
-// side of the barrier.
-__device__ __forceinline__ void barrier_no_fence() {
-  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-}
-
-__device__ __forceinline__ uint4 ld_global16(const void* p) { return *reinterpret_cast<const uint4*>(p); }
-
-template <typename T, typename S>
-__device__ __forceinline__ T bitcast(const S& s) {
-  static_assert(sizeof(T) == sizeof(S), "size");
-  T t;
-  __builtin_memcpy(&t, &s, sizeof(T));
-  return t;
-}
 
 struct Item {
   int head;
@@ -93,17 +54,6 @@ struct Item {
   const uint32_t* runs;  // interval form: packed runs lo | hi << 16
   int n;                 // key blocks to visit (index list, anchor), or runs (interval form)
 };
-
-// Logical item of grid block b. Workgroups go round-robin over the 8 XCDs;
-// each run of 8*G grid blocks gives XCD x the G consecutive items
-// [run*8G + x*G, run*8G + (x+1)*G). The last, partial run keeps grid order.
-__device__ __forceinline__ int64_t xcd_item(int64_t b, int64_t total, int G) {
-  if (G <= 0) return b;
-  const int64_t run = b / (8 * (int64_t)G);
-  if ((run + 1) * 8 * (int64_t)G > total) return b;
-  const int64_t s = b - run * 8 * (int64_t)G;
-  return run * 8 * (int64_t)G + (s % 8) * G + s / 8;
-}
 
 __device__ __forceinline__ Item decode_item(const AttnParams& p, int64_t item) {
   Item it;
@@ -146,22 +96,6 @@ __device__ __forceinline__ int query_token(const AttnParams& p, const Item& it, 
   const int ai = rem / p.C;
   const int c = rem - ai * p.C;
   return (f * p.R + p.anchors[ai]) * p.C + c;
-}
-
-// One 16-byte HBM -> LDS copy (global_load_lds_dwordx4): lane l's chunk lands
-// in slot l of the 64-slot window at `lds` (LDS address = M0 + 16 * lane).
-// The source is a uniform base (SGPR pair) plus this lane's 32-bit offset.
-//
-// Issued as inline assembly on purpose. The compiler does not know which LDS
-// bytes the copy writes, so after the builtin form it turns every later LDS
-// operand wait into lgkmcnt(0), serialising the MFMA operand reads. The
-// hardware counts these copies in vmcnt only; the kernel waits for them
-// explicitly (wait_vmcnt) before the barrier that publishes a stage. The
-// statement has no register outputs, M0 is set inside it, and the memory
-// clobber keeps it after the barrier that frees the destination buffer.
-__device__ __forceinline__ void dma16(const char* base, uint32_t off, uint4* lds) {
-  const uint32_t m0 = (uint32_t)(uintptr_t)(lds_void*)lds;
-  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2" :: "s"(m0), "v"(off), "s"(base) : "memory");
 }
 
 template <int D, int BLK>

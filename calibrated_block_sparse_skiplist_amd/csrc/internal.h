@@ -65,6 +65,22 @@ struct BcastParams {
   int32_t heads[CALIBATT_MAX_HEADS];
 };
 
+// Block energies of selected heads for one prompt: one work item per
+// (head, query block) in head-major order.
+struct EnergyParams {
+  const void* q;
+  const void* k;
+  float* energy;            // [H][nb][nb]
+  int64_t head_stride;      // N * d elements
+  int32_t N;
+  int32_t nb;
+  float scale;
+  float scale_log2;
+  int32_t dtype_f32;        // 1: fp32 inputs, 0: bf16
+  int32_t n_heads;
+  int32_t heads[CALIBATT_MAX_HEADS];
+};
+
 inline int64_t attn_items(const AttnParams& p) {
   return (int64_t)p.n_anchor * p.anchor_tiles + (int64_t)p.n_sparse * p.nb;
 }
@@ -73,6 +89,10 @@ inline int64_t attn_items(const AttnParams& p) {
 hipError_t launch_attn_bf16(const AttnParams& p, int d, int blk, hipStream_t s);
 hipError_t launch_attn_f32(const AttnParams& p, int d, int blk, hipStream_t s);
 hipError_t launch_broadcast(const BcastParams& p, hipStream_t s);
+hipError_t launch_energy(const EnergyParams& p, int d, int blk, hipStream_t s);
+hipError_t launch_select(const float* energy, int64_t rows, int nb, unsigned long long need, uint8_t* mask,
+                         int32_t* counts, hipStream_t s);
+hipError_t launch_keep(const int32_t* counts, int64_t n, int32_t k_min, uint8_t* out, hipStream_t s);
 
 hipError_t launch_compile_count_scan(const uint8_t* masks, int64_t rows, int nb, int64_t* row_ptr,
                                      hipStream_t s);

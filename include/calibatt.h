@@ -217,15 +217,65 @@ calibatt_status_t calibatt_layer_dispatch_iv(const void* q, const void* k, const
                                              const uint8_t* rep_flags, int32_t F, int32_t R, int32_t C,
                                              const int32_t* anchor_rows, int32_t k_anchors, void* stream);
 
+/*
+ * ---- Offline calibration (produces the masks compiled above) ----
+ *
+ * Block energies of one calibration prompt ([Notes] Key Design 1, Eq. 5; Key
+ * Design 4: accumulated without materialising the attention matrix). For each
+ * listed head h, query block r and key block c:
+ *   E[h][r][c] = (1/|I_r|) * sum_{i in I_r} sum_{j in J_c} P[i][j],
+ *   P = softmax over all N keys of scale * Q[h][i] . K[h][j].
+ * The average is over the block's actual query count |I_r| (B for every full
+ * block), so each row of E sums to one, also for a partial last block.
+ *   q, k      [H][N][d] (bf16 or fp32), device, read-only.
+ *   B         64 or 128 (query and key block size); nb = ceil(N/B) <= CALIBATT_MAX_NB.
+ *   energy    float [H][nb][nb], device; rows of the listed heads are written.
+ *   heads     host int32 [n_heads] or NULL for all heads.
+ * Asynchronous; the kernel reads K twice (one pass for each query's
+ * log-sum-exp, one for the sums). calibatt_set_kernel_events applies to it.
+ */
+calibatt_status_t calibatt_block_energy(const void* q, const void* k, int32_t H, int32_t N, int32_t d,
+                                        calibatt_dtype_t dtype, float scale, int32_t B, float* energy,
+                                        const int32_t* heads, int32_t n_heads, void* stream);
+
+/*
+ * Per-prompt selection ([Notes] Key Design 1): for every row of `energy`
+ * (rows x nb, device, finite and >= 0), sort the energies in descending order
+ * (ties to the lower key block) and keep the shortest prefix whose cumulative
+ * mass reaches tau (>=). The cumulative mass is summed exactly in 2^-48 fixed
+ * point: each energy counts floor(E * 2^48) units against ceil(tau * 2^48), so
+ * the decision does not depend on summation order. A row that never reaches
+ * tau keeps every block. 0 <= tau <= 1.
+ *   mask      uint8 [rows][nb], device, written (1 = keep), or NULL.
+ *   counts    int32 [rows][nb], device, or NULL: incremented by the mask
+ *             (accumulates the selections of the calibration prompts).
+ * At least one of mask and counts must be non-NULL. Asynchronous.
+ */
+calibatt_status_t calibatt_select_blocks(const float* energy, int64_t rows, int32_t nb, float tau,
+                                         uint8_t* mask, int32_t* counts, void* stream);
+
+/*
+ * Cross-prompt aggregation ([Notes] Key Design 2, Eq. 8-9; A Worked Example:
+ * 64 prompts at rho = 0.5 keep blocks selected at least 32 times):
+ *   mask[i] = (counts[i] / n_prompts >= rho), evaluated exactly as
+ *   counts[i] >= ceil(rho * n_prompts).
+ *   counts    int32 [n], device (from calibatt_select_blocks over the prompts).
+ *   mask      uint8 [n], device, written; e.g. the [T][L][H][nb][nb] slice of
+ *             a dictionary for calibatt_compile_skiplist / _intervals.
+ * n_prompts >= 1, 0 <= rho <= 1. Asynchronous.
+ */
+calibatt_status_t calibatt_keep_frequency(const int32_t* counts, int64_t n, int32_t n_prompts, float rho,
+                                          uint8_t* mask, void* stream);
+
 /* Message for the last non-OK status returned on this thread ("" if none). */
 const char* calibatt_last_error(void);
 
 /*
- * Timing hook for benchmarks: the next attention launch made on this thread
- * by calibatt_block_sparse_attn(_iv), calibatt_anchor_attn or
- * calibatt_layer_dispatch(_iv) records hipEvent_t `begin` right before the
- * attention kernel and `end` right after it, on the same stream; the hook
- * then clears itself. Pass NULL, NULL to clear it explicitly.
+ * Timing hook for benchmarks: the next attention or energy launch made on
+ * this thread by calibatt_block_sparse_attn(_iv), calibatt_anchor_attn,
+ * calibatt_layer_dispatch(_iv) or calibatt_block_energy records hipEvent_t
+ * `begin` right before that kernel and `end` right after it, on the same
+ * stream; the hook then clears itself. Pass NULL, NULL to clear it explicitly.
  */
 void calibatt_set_kernel_events(void* begin, void* end);
 

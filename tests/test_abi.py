@@ -163,6 +163,37 @@ def test_compile_intervals_rejects():
     assert f(P, 1, 1, 1, 100, 10, None, None, 0, None, ctypes.byref(n), None) == INVALID
 
 
+@pytest.mark.parametrize("kw,msg", [
+    (dict(q=None), "non-NULL"), (dict(energy=None), "non-NULL"), (dict(d=32), "d = 32"), (dict(B=96), "block size"),
+    (dict(scale=-1.0), "scale"), (dict(N=4097 * 64, B=64), "nb exceeds"), (dict(dtype=5), "dtype"),
+])
+def test_block_energy_rejects(kw, msg):
+    a = dict(q=P, k=P, H=2, N=1000, d=128, dtype=cal.BF16, scale=0.088, B=128, energy=P)
+    a.update(kw)
+    st = lib.calibatt_block_energy(a["q"], a["k"], a["H"], a["N"], a["d"], a["dtype"], a["scale"], a["B"],
+                                   a["energy"], None, 0, None)
+    assert st == INVALID and msg in cal.last_error()
+    bad = np.array([2], dtype=np.int32)
+    assert lib.calibatt_block_energy(P, P, 2, 1000, 128, cal.BF16, 0.088, 128, P, bad.ctypes.data, 1, None) == INVALID
+
+
+@pytest.mark.parametrize("args,msg", [
+    ((None, 4, 8, 0.5, P, None), "energy"), ((P, 4, 8, 0.5, None, None), "both NULL"), ((P, -1, 8, 0.5, P, None), "rows"),
+    ((P, 4, 0, 0.5, P, None), "nb"), ((P, 4, 4097, 0.5, P, None), "nb"), ((P, 4, 8, 1.5, P, None), "tau"),
+    ((P, 4, 8, float("nan"), P, None), "tau"), ((P, 4, 8, -0.1, None, P), "tau"),
+])
+def test_select_blocks_rejects(args, msg):
+    assert lib.calibatt_select_blocks(*args, None) == INVALID and msg in cal.last_error()
+
+
+@pytest.mark.parametrize("args,msg", [
+    ((None, 4, 64, 0.5, P), "non-NULL"), ((P, 4, 64, 0.5, None), "non-NULL"), ((P, -1, 64, 0.5, P), "n must"),
+    ((P, 4, 0, 0.5, P), "n_prompts"), ((P, 4, 64, 1.01, P), "rho"), ((P, 4, 64, float("inf"), P), "rho"),
+])
+def test_keep_frequency_rejects(args, msg):
+    assert lib.calibatt_keep_frequency(*args, None) == INVALID and msg in cal.last_error()
+
+
 def test_product_path_does_not_import_the_oracle():
     import sys
     pkg = os.path.join(ROOT, "calibrated_block_sparse_skiplist_amd")

@@ -27,7 +27,7 @@ __all__ = [
     "LayerConfig", "CONFIGS", "get_config", "bf16_bits", "bf16_to_f32",
     "make_qkv", "block_frame_distance", "make_masks", "make_rep_flags",
     "equally_spaced_anchor_rows", "Workload", "make_workload",
-    "make_dictionary_workload",
+    "make_dictionary_workload", "make_calibration_prompts",
 ]
 
 
@@ -308,3 +308,43 @@ def make_dictionary_workload(sparsity: float, rep_fraction: float, L: int = 40,
         if cfg.n_rep:
             flags[0, l, rrng.choice(H, size=cfg.n_rep, replace=False)] = 1
     return cfg, masks, flags
+
+
+# ---------------------------------------------------------------------------
+# Calibration prompts (inputs of the offline block-energy calibration)
+# ---------------------------------------------------------------------------
+def make_calibration_prompts(N: int, d: int, F: int, R: int, C: int, H: int, n_prompts: int,
+                             dtype: str = "bf16", seed: int = 4000, strength: float = 1.3):
+    """Q and K [P, H, N, d] of P synthetic calibration prompts.
+
+    Each prompt draws its own standard-normal Q and K noise; every prompt adds
+    the same position code (per head: random frequencies along frame, row and
+    column, as cos/sin pairs scaled by `strength`) to both Q and K. The code
+    makes q_i . k_j large for nearby positions, so attention concentrates near
+    the query as it does in video transformers, and the pattern is stable
+    across prompts while the details are not. bf16 configs return uint16 bit
+    patterns, fp32 configs float32 arrays.
+    """
+    if F * R * C != N:
+        raise ValueError("N must equal F*R*C")
+    code_rng = np.random.Generator(np.random.PCG64(seed))
+    n = np.arange(N)
+    pos = np.stack([n // (R * C), (n // C) % R, n % C]).astype(np.float64)     # [3, N]
+    extent = np.array([F, R, C], dtype=np.float64)
+    code = np.empty((H, N, d), dtype=np.float32)
+    for h in range(H):
+        axis = code_rng.integers(0, 3, size=d // 2)
+        freq = code_rng.uniform(0.2, 3.0, size=d // 2) * 2.0 * np.pi / extent[axis] * code_rng.integers(1, 4, size=d // 2)
+        ang = pos[axis] * freq[:, None]                                       # [d/2, N]
+        code[h, :, 0::2] = (strength * np.cos(ang)).T
+        code[h, :, 1::2] = (strength * np.sin(ang)).T
+    qs, ks = [], []
+    for p in range(n_prompts):
+        rng = np.random.Generator(np.random.PCG64(seed + 1 + p))
+        q = rng.standard_normal((H, N, d), dtype=np.float32) + code
+        k = rng.standard_normal((H, N, d), dtype=np.float32) + code
+        if dtype == "bf16":
+            q, k = bf16_bits(q), bf16_bits(k)
+        qs.append(q)
+        ks.append(k)
+    return np.stack(qs), np.stack(ks)
