@@ -64,6 +64,12 @@ attention outputs have no external worked example; no function here is
     section), and the cross-prompt keep frequency thresholded at rho
     (Eq. 8-9, [Notes] Key Design 2; A Worked Example).
 
+``repetition.row_similarity`` / ``repetition_mean`` / ``repetition_flags``
+    The spatial-repetition branch of calibration ([Notes] Key Design 3): the
+    cosine similarity of each spatial row's flattened attention with its
+    nearest anchor row's, averaged over frames, rows and prompts, and the
+    head flagged when the mean exceeds the threshold.
+
 Readings of points the pages leave open are listed in the module docstrings
 where they are applied (empty rows, partial last block, anchor ties, token
 order, broadcast unit).
@@ -72,7 +78,8 @@ from .skiplist import compile_intervals, compile_skiplist, intervals_to_dense, s
 from .attention import (block_sparse_head, anchor_head, nearest_anchor_rows,
                         layer_forward, block_tokens)
 from .calibration import block_energy, keep_counts, keep_frequency_mask, select_blocks
+from .repetition import repetition_flags, repetition_mean, row_similarity
 
 __all__ = ["compile_intervals", "compile_skiplist", "intervals_to_dense", "skiplist_to_dense", "block_sparse_head", "anchor_head",
            "nearest_anchor_rows", "layer_forward", "block_tokens", "block_energy", "keep_counts",
-           "keep_frequency_mask", "select_blocks"]
+           "keep_frequency_mask", "select_blocks", "repetition_flags", "repetition_mean", "row_similarity"]
