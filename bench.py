@@ -249,7 +249,9 @@ def dictionary_sweep(args):
 def calibration_bench(args):
     """Offline calibration of one layer at the Wan-720p shape: per prompt, block energies of all 40 heads
     (calibatt_block_energy) and their top-tau selection accumulated into keep counts
-    (calibatt_select_blocks); then the keep-frequency mask (calibatt_keep_frequency)."""
+    (calibatt_select_blocks); then the keep-frequency mask (calibatt_keep_frequency). The
+    spatial-repetition branch: per prompt, row similarities of all heads (calibatt_spatial_similarity,
+    log-sum-exp pass + similarity kernel), then the flags (calibatt_repetition_flags)."""
     import torch
     import workloads
     import calibrated_block_sparse_skiplist_amd as cal
@@ -286,6 +288,34 @@ def calibration_bench(args):
     b.record(stream)
     torch.cuda.synchronize()
     keep_ms = a.elapsed_time(b)
+    # spatial-repetition branch: per prompt, row similarities of all heads; then the flags
+    anchors = workloads.equally_spaced_anchor_rows(cfg.R, cfg.n_anchor)
+    lse_work = torch.empty((H, N), dtype=torch.float32, device=dev)
+    sims = torch.empty((args.prompts, H, cfg.F, cfg.R), dtype=torch.float32, device=dev)
+    cal.calibatt_spatial_similarity(qd, kd, cfg.F, cfg.R, cfg.C, anchors, lse_work, sims[0], stream=stream)
+    torch.cuda.synchronize()
+    sim_ms, simk_ms = [], []
+    for p in range(args.prompts):
+        a, b, c, e = (torch.cuda.Event(enable_timing=True) for _ in range(4))
+        a.record(stream)
+        b.record(stream)
+        c.record(stream)
+        cal.calibatt_set_kernel_events(b.cuda_event, c.cuda_event)
+        cal.calibatt_spatial_similarity(qd, kd, cfg.F, cfg.R, cfg.C, anchors, lse_work, sims[p], stream=stream)
+        e.record(stream)
+        torch.cuda.synchronize()
+        sim_ms.append(a.elapsed_time(e))
+        simk_ms.append(b.elapsed_time(c))
+    flags = torch.empty((H,), dtype=torch.uint8, device=dev)
+    mean = torch.empty((H,), dtype=torch.float32, device=dev)
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record(stream)
+    cal.calibatt_repetition_flags(sims, anchors, 0.87, flags=flags, mean=mean, stream=stream)
+    b.record(stream)
+    torch.cuda.synchronize()
+    flags_ms = a.elapsed_time(b)
+    sim_flop = 2.0 * d * N * (2 * cfg.C * (cfg.R - len(anchors)) * cfg.F) * H    # row and anchor scores per pair
+
     energy_ms = float(np.mean(e_ms))
     qk_flop = 2.0 * d * N * N * H                  # one QK^T product over all heads
     executed = 2 * qk_flop                         # the kernel computes the scores twice
@@ -301,6 +331,11 @@ def calibration_bench(args):
         "select_rows": H * nb, "nb": nb, "keep_frequency_ms": round(keep_ms, 3),
         "kept_fraction_final_mask": round(float(mask.float().mean().item()), 4),
         "energy_row_sum_max_dev": float((row_sums - 1.0).abs().max().item()),
+        "similarity_ms_per_prompt": round(float(np.mean(sim_ms)), 3),
+        "similarity_kernel_ms": round(float(np.mean(simk_ms)), 3),
+        "similarity_kernel_tflops": round(sim_flop / (float(np.mean(simk_ms)) * 1e-3) / 1e12, 1),
+        "repetition_flags_ms": round(flags_ms, 3),
+        "mean_row_similarity": [round(float(x), 4) for x in mean.cpu().numpy()[:4]],
     }), flush=True)
 
 

@@ -9,6 +9,8 @@ The names follow the C ABI in include/calibatt.h:
 * ``calibatt_layer_dispatch`` (``_iv``) -- one layer-call, per-head choice of path
 * ``calibatt_block_energy`` / ``calibatt_select_blocks`` / ``calibatt_keep_frequency`` -- offline
   calibration: block energies of a prompt, its top-tau selection, cross-prompt keep frequency
+* ``calibatt_spatial_similarity`` / ``calibatt_repetition_flags`` -- offline calibration: spatial-row
+  similarity to the nearest anchor row, and the per-head repetition flags
 
 All computation happens in the library's HIP kernels; this package only
 marshals arguments. Importing it fails if the library has not been built.
@@ -17,12 +19,14 @@ from ._lib import (BF16, F32, CalibattError, IntervalList, IntervalListView, Ski
                    calibatt_anchor_attn, calibatt_block_energy, calibatt_block_sparse_attn,
                    calibatt_block_sparse_attn_iv, calibatt_keep_frequency, calibatt_select_blocks,
                    calibatt_compile_intervals, calibatt_compile_skiplist, calibatt_layer_dispatch,
-                   calibatt_layer_dispatch_iv, calibatt_set_kernel_events, calibatt_version,
+                   calibatt_layer_dispatch_iv, calibatt_repetition_flags, calibatt_set_kernel_events,
+                   calibatt_spatial_similarity, calibatt_version,
                    compile_intervals, compile_skiplist, last_error)
 
 __all__ = ["BF16", "F32", "CalibattError", "IntervalList", "IntervalListView", "SkipList", "SkipListView",
            "calibatt_anchor_attn", "calibatt_block_energy", "calibatt_block_sparse_attn",
            "calibatt_block_sparse_attn_iv", "calibatt_keep_frequency", "calibatt_select_blocks",
            "calibatt_compile_intervals", "calibatt_compile_skiplist", "calibatt_layer_dispatch",
-           "calibatt_layer_dispatch_iv", "calibatt_set_kernel_events", "calibatt_version",
+           "calibatt_layer_dispatch_iv", "calibatt_repetition_flags", "calibatt_set_kernel_events",
+           "calibatt_spatial_similarity", "calibatt_version",
            "compile_intervals", "compile_skiplist", "last_error"]

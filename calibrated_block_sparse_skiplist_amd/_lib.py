@@ -24,6 +24,7 @@ EXPORTED = (
     "calibatt_compile_skiplist", "calibatt_block_sparse_attn", "calibatt_anchor_attn",
     "calibatt_layer_dispatch", "calibatt_compile_intervals", "calibatt_block_sparse_attn_iv",
     "calibatt_layer_dispatch_iv", "calibatt_block_energy", "calibatt_select_blocks", "calibatt_keep_frequency",
+    "calibatt_spatial_similarity", "calibatt_repetition_flags",
     "calibatt_last_error", "calibatt_set_kernel_events", "calibatt_version",
 )
 
@@ -86,6 +87,11 @@ def _load():
     lib.calibatt_select_blocks.restype = i32
     lib.calibatt_keep_frequency.argtypes = [vp, i64, i32, f32, vp, vp]
     lib.calibatt_keep_frequency.restype = i32
+    lib.calibatt_spatial_similarity.argtypes = [vp, vp, i32, i32, i32, i32, f32, i32, i32, i32, vp, i32, vp, vp,
+                                                vp, i32, vp]
+    lib.calibatt_spatial_similarity.restype = i32
+    lib.calibatt_repetition_flags.argtypes = [vp, i32, i32, i32, i32, vp, i32, f32, vp, vp, vp]
+    lib.calibatt_repetition_flags.restype = i32
     lib.calibatt_last_error.argtypes = []
     lib.calibatt_last_error.restype = ctypes.c_char_p
     lib.calibatt_set_kernel_events.argtypes = [vp, vp]
@@ -320,6 +326,26 @@ def calibatt_keep_frequency(counts, n_prompts: int, rho: float, mask, stream=Non
     """mask = counts / n_prompts >= rho (elementwise, exact)."""
     _check(lib.calibatt_keep_frequency(_ptr(counts), counts.numel(), n_prompts, float(rho), _ptr(mask),
                                        _stream(stream)))
+
+
+def calibatt_spatial_similarity(q, k, F: int, R: int, C: int, anchor_rows, lse_work, row_sim, heads=None,
+                                scale: float | None = None, stream=None) -> None:
+    """Row similarities [H, F, R] (float32 device tensor) of one prompt; lse_work: float32 [H, N] workspace."""
+    H, N, d = q.shape
+    scale = float(np.float32(1.0 / np.sqrt(d))) if scale is None else scale
+    aarr, ka = _host_i32(anchor_rows)
+    harr, nh = _host_i32(heads)
+    _check(lib.calibatt_spatial_similarity(_ptr(q), _ptr(k), H, N, d, _dtype_code(q), scale, F, R, C,
+                                           aarr.ctypes.data, ka, _ptr(lse_work), _ptr(row_sim),
+                                           harr.ctypes.data if harr is not None else None, nh, _stream(stream)))
+
+
+def calibatt_repetition_flags(row_sim, anchor_rows, threshold: float, flags=None, mean=None, stream=None) -> None:
+    """row_sim: float32 device tensor [P, H, F, R]; writes flags (uint8 [H]) and/or mean (float32 [H])."""
+    P, H, F, R = row_sim.shape
+    aarr, ka = _host_i32(anchor_rows)
+    _check(lib.calibatt_repetition_flags(_ptr(row_sim), P, H, F, R, aarr.ctypes.data, ka, float(threshold),
+                                         _ptr(flags), _ptr(mean), _stream(stream)))
 
 
 def calibatt_set_kernel_events(begin, end) -> None:

@@ -71,6 +71,7 @@ struct EnergyParams {
   const void* q;
   const void* k;
   float* energy;            // [H][nb][nb]
+  float* lse2;              // [H][N] log2-sum-exp per query (log-sum-exp pass only)
   int64_t head_stride;      // N * d elements
   int32_t N;
   int32_t nb;
@@ -79,6 +80,29 @@ struct EnergyParams {
   int32_t dtype_f32;        // 1: fp32 inputs, 0: bf16
   int32_t n_heads;
   int32_t heads[CALIBATT_MAX_HEADS];
+};
+
+// Spatial-row similarities of selected heads for one prompt: one work item
+// per (head, frame, spatial row).
+struct SimParams {
+  const void* q;
+  const void* k;
+  const float* lse2;        // [H][N] log2-sum-exp per query (from launch_row_lse)
+  float* row_sim;           // [H][F][R]
+  int64_t head_stride;      // N * d elements
+  int32_t N;
+  int32_t F, R, C, ka;
+  float scale;
+  float scale_log2;
+  int32_t n_heads;
+  int32_t anchors[CALIBATT_MAX_ANCHORS];
+  int32_t heads[CALIBATT_MAX_HEADS];
+};
+
+struct RepFlagParams {
+  int32_t anchors[CALIBATT_MAX_ANCHORS];
+  int32_t ka;
+  float threshold;
 };
 
 inline int64_t attn_items(const AttnParams& p) {
@@ -90,6 +114,10 @@ hipError_t launch_attn_bf16(const AttnParams& p, int d, int blk, hipStream_t s);
 hipError_t launch_attn_f32(const AttnParams& p, int d, int blk, hipStream_t s);
 hipError_t launch_broadcast(const BcastParams& p, hipStream_t s);
 hipError_t launch_energy(const EnergyParams& p, int d, int blk, hipStream_t s);
+hipError_t launch_row_lse(const EnergyParams& p, int d, hipStream_t s);   // 128-query tiles
+hipError_t launch_similarity(const SimParams& p, int d, bool f32, hipStream_t s);
+hipError_t launch_rep_flags(const float* sims, int P, int H, int F, int R, const RepFlagParams& q, uint8_t* flags,
+                            float* mean, hipStream_t s);
 hipError_t launch_select(const float* energy, int64_t rows, int nb, unsigned long long need, uint8_t* mask,
                          int32_t* counts, hipStream_t s);
 hipError_t launch_keep(const int32_t* counts, int64_t n, int32_t k_min, uint8_t* out, hipStream_t s);

@@ -267,13 +267,53 @@ calibatt_status_t calibatt_select_blocks(const float* energy, int64_t rows, int3
 calibatt_status_t calibatt_keep_frequency(const int32_t* counts, int64_t n, int32_t n_prompts, float rho,
                                           uint8_t* mask, void* stream);
 
+/*
+ * Spatial-repetition detection, per prompt ([Notes] Key Design 3: the
+ * attention of each spatial row, flattened, is compared by cosine similarity
+ * with that of its nearest anchor row within the frame). For every listed
+ * head h, frame f and spatial row r with nearest anchor a (ties to the smaller
+ * anchor row):
+ *   row_sim[h][f][r] = <P_r, P_a> / (|P_r| |P_a|),
+ *   <P_r, P_a> = sum_{c < C} sum_{j < N} P[(f*R + r)*C + c][j] * P[(f*R + a)*C + c][j],
+ * P = softmax over all N keys of scale * Q[h][i] . K[h][j]; anchor rows get 1.
+ *   q, k        [H][N][d] (bf16 or fp32), device, read-only; N = F*R*C.
+ *   anchor_rows host int32 [k_anchors], strictly ascending in [0, R); 1 <= k < R.
+ *   lse_work    float [H][N], device, caller-owned workspace: overwritten (for
+ *               the listed heads) with each query's base-2 log-sum-exp of
+ *               scale * q . k over all keys.
+ *   row_sim     float [H][F][R], device, written for the listed heads.
+ *   heads       host int32 [n_heads] or NULL for all heads.
+ * Asynchronous. calibatt_set_kernel_events times the similarity kernel.
+ */
+calibatt_status_t calibatt_spatial_similarity(const void* q, const void* k, int32_t H, int32_t N, int32_t d,
+                                              calibatt_dtype_t dtype, float scale, int32_t F, int32_t R,
+                                              int32_t C, const int32_t* anchor_rows, int32_t k_anchors,
+                                              float* lse_work, float* row_sim, const int32_t* heads,
+                                              int32_t n_heads, void* stream);
+
+/*
+ * Repetition flags ([Notes] Key Design 3: the similarities are averaged over
+ * frames, rows and calibration prompts; a head is repetitive only when the
+ * mean exceeds the threshold, 0.87 by default). The mean runs over the
+ * non-anchor rows of every frame of every prompt, accumulated in double in a
+ * fixed order; flag = mean > threshold (strict).
+ *   row_sim     float [n_prompts][H][F][R], device (row_sim of each prompt).
+ *   flags       uint8 [H], device, written (1 = repetitive), or NULL.
+ *   mean        float [H], device, written, or NULL (not both NULL).
+ * Asynchronous.
+ */
+calibatt_status_t calibatt_repetition_flags(const float* row_sim, int32_t n_prompts, int32_t H, int32_t F,
+                                            int32_t R, const int32_t* anchor_rows, int32_t k_anchors,
+                                            float threshold, uint8_t* flags, float* mean, void* stream);
+
 /* Message for the last non-OK status returned on this thread ("" if none). */
 const char* calibatt_last_error(void);
 
 /*
  * Timing hook for benchmarks: the next attention or energy launch made on
  * this thread by calibatt_block_sparse_attn(_iv), calibatt_anchor_attn,
- * calibatt_layer_dispatch(_iv) or calibatt_block_energy records hipEvent_t
+ * calibatt_layer_dispatch(_iv), calibatt_block_energy or
+ * calibatt_spatial_similarity records hipEvent_t
  * `begin` right before that kernel and `end` right after it, on the same
  * stream; the hook then clears itself. Pass NULL, NULL to clear it explicitly.
  */

@@ -194,6 +194,35 @@ def test_keep_frequency_rejects(args, msg):
     assert lib.calibatt_keep_frequency(*args, None) == INVALID and msg in cal.last_error()
 
 
+def test_spatial_similarity_rejects():
+    anchors = np.array([2, 7], dtype=np.int32)
+    f = lib.calibatt_spatial_similarity
+    def call(**kw):
+        a = dict(q=P, k=P, H=1, N=600, d=64, dtype=cal.BF16, scale=0.125, F=3, R=10, C=20,
+                 anchors=anchors.ctypes.data, ka=2, lse=P, sim=P)
+        a.update(kw)
+        return f(a["q"], a["k"], a["H"], a["N"], a["d"], a["dtype"], a["scale"], a["F"], a["R"], a["C"],
+                 a["anchors"], a["ka"], a["lse"], a["sim"], None, 0, None)
+    assert call(lse=None) == INVALID and "lse_work" in cal.last_error()
+    assert call(sim=None) == INVALID
+    assert call(N=601) == INVALID and "F*R*C" in cal.last_error()
+    assert call(d=32) == INVALID
+    every = np.arange(10, dtype=np.int32)
+    assert call(anchors=every.ctypes.data, ka=10) == INVALID and "every row" in cal.last_error()
+
+
+def test_repetition_flags_rejects():
+    anchors = np.array([1], dtype=np.int32)
+    f = lib.calibatt_repetition_flags
+    assert f(None, 1, 1, 1, 4, anchors.ctypes.data, 1, 0.87, P, None, None) == INVALID
+    assert f(P, 1, 1, 1, 4, anchors.ctypes.data, 1, 0.87, None, None, None) == INVALID
+    assert f(P, 0, 1, 1, 4, anchors.ctypes.data, 1, 0.87, P, None, None) == INVALID
+    assert f(P, 1, 1, 1, 1, anchors.ctypes.data, 1, 0.87, P, None, None) == INVALID
+    bad = np.array([3, 1], dtype=np.int32)
+    assert f(P, 1, 1, 1, 4, bad.ctypes.data, 2, 0.87, P, None, None) == INVALID
+    assert f(P, 1, 1, 1, 4, anchors.ctypes.data, 1, float("nan"), P, None, None) == INVALID
+
+
 def test_product_path_does_not_import_the_oracle():
     import sys
     pkg = os.path.join(ROOT, "calibrated_block_sparse_skiplist_amd")
