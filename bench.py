@@ -59,6 +59,11 @@ def parse_args():
                     help="offline calibration at the Wan-720p shape: block energies of one prompt (all 40 heads), "
                          "top-tau selection, keep frequency (one JSON line)")
     ap.add_argument("--prompts", type=int, default=3, help="calibration prompts timed")
+    ap.add_argument("--dictionary-run", action="store_true",
+                    help="a whole denoising run's dictionary at the Wan-720p shape (50 timesteps x 40 layers x "
+                         "40 heads) resident on the GPU: compile both list forms, account memory, and stream "
+                         "layer calls through sampled timesteps (one JSON line)")
+    ap.add_argument("--run-steps", default="0,25,49", help="timesteps whose 40 layer calls are timed")
     return ap.parse_args()
 
 
@@ -339,6 +344,86 @@ def calibration_bench(args):
     }), flush=True)
 
 
+def dictionary_run(args):
+    """Wan-720p denoising-run dictionary (T=50, L=40, H=40): 27.9 GB of block masks generated on the GPU,
+    compiled into index lists and into runs in one call each; memory of each form; then every layer call
+    of the chosen timesteps (record (t, l) selected from the resident dictionary), through the runs."""
+    import torch
+    import workloads
+    import calibrated_block_sparse_skiplist_amd as cal
+    T, L, H = 50, 40, 40
+    dev = torch.device("cuda")
+    stream = torch.cuda.current_stream()
+    t0 = time.perf_counter()
+    cfg, masks, flags = workloads.make_step_dictionary("wan720", T, L, H, dev)
+    torch.cuda.synchronize()
+    gen_s = time.perf_counter() - t0
+    nb = cfg.nb
+    rows = T * L * H * nb
+    mask_bytes = masks.numel()
+    kept = int(torch.count_nonzero(masks).item())
+
+    def timed(fn, reps=3):
+        fn()
+        torch.cuda.synchronize()
+        a = time.perf_counter()
+        for _ in range(reps):
+            fn()
+        torch.cuda.synchronize()
+        return (time.perf_counter() - a) * 1e3 / reps
+
+    il = cal.compile_intervals(masks, cfg.N, cfg.B)
+    iv_ms = timed(lambda: cal.calibatt_compile_intervals(masks, T, L, H, cfg.N, cfg.B, il.iv_ptr, il.iv,
+                                                         il.iv.numel(), il.order, stream))
+    sl = cal.compile_skiplist(masks, cfg.N, cfg.B)
+    csr_ms = timed(lambda: cal.calibatt_compile_skiplist(masks, T, L, H, cfg.N, cfg.B, sl.row_ptr, sl.col_idx,
+                                                         sl.col_idx.numel(), sl.order, stream))
+    n_iv, nnz = il.n_iv, sl.nnz
+    # block sizes for the work of each record
+    sizes = torch.from_numpy(block_sizes(cfg.N, cfg.B)).to(dev, torch.float64)
+    tok = sizes[:, None] * sizes[None, :]
+    del sl
+    torch.cuda.empty_cache()
+
+    import workloads as W
+    q, k, v = W.make_qkv(cfg)
+    qd, kd, vd = (torch.from_numpy(x.view(np.int16)).view(torch.bfloat16).to(dev) for x in (q, k, v))
+    del q, k, v
+    o = torch.empty_like(qd)
+    anchors = W.equally_spaced_anchor_rows(cfg.R, cfg.n_anchor)
+    scale = float(np.float32(1.0 / np.sqrt(cfg.d)))
+    per_step = []
+    for t in [int(x) for x in args.run_steps.split(",")]:
+        cal.calibatt_layer_dispatch_iv(qd, kd, vd, o, None, il, t, 0, flags, cfg.F, cfg.R, cfg.C, anchors,
+                                       scale=scale, stream=stream)
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        a.record(stream)
+        for l in range(L):
+            cal.calibatt_layer_dispatch_iv(qd, kd, vd, o, None, il, t, l, flags, cfg.F, cfg.R, cfg.C, anchors,
+                                           scale=scale, stream=stream)
+        b.record(stream)
+        torch.cuda.synchronize()
+        ms = a.elapsed_time(b)
+        flop = 0.0
+        for l in range(L):
+            sp = torch.from_numpy(flags[t, l] == 0).to(dev)
+            flop += float(4 * cfg.d * (tok[None] * masks[t, l][sp].to(torch.float64)).sum().item())
+            flop += float((~sp).sum().item()) * anchor_head_flops(cfg.F, len(anchors), cfg.C, cfg.N, cfg.d)
+        per_step.append({"t": t, "layers": L, "ms_total": round(ms, 2), "ms_per_layer": round(ms / L, 3),
+                         "kept_fraction": round(float(masks[t].float().mean().item()), 4),
+                         "tflops": round(flop / (ms * 1e-3) / 1e12, 1)})
+    print(json.dumps({
+        "mode": "dictionary_run", "workload": "wan720 shape, 50 timesteps x 40 layers x 40 heads",
+        "mask_generation_s": round(gen_s, 2), "records": T * L * H, "rows": rows, "nb": nb,
+        "kept_blocks": kept, "kept_fraction": round(kept / mask_bytes, 4), "runs": n_iv,
+        "bytes": {"masks": mask_bytes, "index_form": 8 * (rows + 1) + 4 * nnz + 4 * rows,
+                  "interval_form": 8 * (rows + 1) + 4 * n_iv + 4 * rows},
+        "compile_ms": {"index_form": round(csr_ms, 2), "interval_form": round(iv_ms, 2)},
+        "compile_GBps_masks_read_twice": round(2 * mask_bytes / (iv_ms * 1e-3) / 1e9, 1),
+        "layer_calls": per_step}), flush=True)
+
+
 def main():
     args = parse_args()
     if args.gpus != 1:
@@ -351,6 +436,9 @@ def main():
         return
     if args.calibration:
         calibration_bench(args)
+        return
+    if args.dictionary_run:
+        dictionary_run(args)
         return
     if args.copy_calib:
         src = torch.empty(1 << 28, dtype=torch.float32, device="cuda")

@@ -27,7 +27,7 @@ __all__ = [
     "LayerConfig", "CONFIGS", "get_config", "bf16_bits", "bf16_to_f32",
     "make_qkv", "block_frame_distance", "make_masks", "make_rep_flags",
     "equally_spaced_anchor_rows", "Workload", "make_workload",
-    "make_dictionary_workload", "make_calibration_prompts",
+    "make_dictionary_workload", "make_calibration_prompts", "make_step_dictionary",
 ]
 
 
@@ -348,3 +348,53 @@ def make_calibration_prompts(N: int, d: int, F: int, R: int, C: int, H: int, n_p
         qs.append(q)
         ks.append(k)
     return np.stack(qs), np.stack(ks)
+
+
+# ---------------------------------------------------------------------------
+# Full denoising-run dictionary (all timesteps), generated on the GPU
+# ---------------------------------------------------------------------------
+def step_keep_fraction(T: int, L: int, H: int, seed: int = 6000) -> np.ndarray:
+    """Target kept-block fraction per (t, l, h): denser at early (noisy) steps.
+
+    0.55 at t = 0 falling linearly to 0.25 at the last step, times a per-(l, h)
+    factor in [0.7, 1.3], clipped to [0.05, 0.95].
+    """
+    rng = np.random.Generator(np.random.PCG64(seed))
+    base = 0.55 - 0.30 * np.arange(T) / max(T - 1, 1)
+    jitter = rng.uniform(0.7, 1.3, size=(1, L, H))
+    return np.clip(base[:, None, None] * jitter, 0.05, 0.95)
+
+
+def make_step_dictionary(key: str, T: int, L: int, H: int, device, seed: int = 6000):
+    """Masks [T, L, H, nb, nb] (uint8 torch tensor on `device`) and flags [T, L, H] (numpy uint8).
+
+    Per (t, l, h) with keep fraction k: blocks within a frame distance of
+    round(0.4 * k * F) are kept (temporal band), every other block with
+    probability 0.3 * k (far blocks), and the diagonal always; the realized
+    kept fraction comes out close to k. The random draws
+    come from a seeded torch generator on `device`, one (t, l) slice at a
+    time. 20% of the heads of every (t, l) are flagged repetitive.
+    """
+    import torch
+    cfg = get_config(key)
+    nb = cfg.nb
+    dist = torch.from_numpy(block_frame_distance(cfg.N, cfg.B, cfg.F, cfg.R, cfg.C)).to(device)
+    eye = torch.eye(nb, dtype=torch.bool, device=device)
+    keep = step_keep_fraction(T, L, H, seed)
+    gen = torch.Generator(device=device)
+    gen.manual_seed(seed)
+    masks = torch.empty((T, L, H, nb, nb), dtype=torch.uint8, device=device)
+    for t in range(T):
+        for l in range(L):
+            k = torch.from_numpy(keep[t, l]).to(device=device, dtype=torch.float32)
+            band = torch.round(0.4 * k * cfg.F).to(torch.int64)
+            u = torch.rand((H, nb, nb), generator=gen, device=device)
+            m = (dist[None] <= band[:, None, None]) | (u < (0.3 * k)[:, None, None]) | eye[None]
+            masks[t, l] = m.to(torch.uint8)
+    frng = np.random.Generator(np.random.PCG64(seed + 1))
+    flags = np.zeros((T, L, H), dtype=np.uint8)
+    n_rep = max(1, H // 5)
+    for t in range(T):
+        for l in range(L):
+            flags[t, l, frng.choice(H, size=n_rep, replace=False)] = 1
+    return cfg, masks, flags
