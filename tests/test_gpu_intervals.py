@@ -163,3 +163,44 @@ def test_layer_dispatch_over_runs_matches_index_lists(key):
     for b in blocks:
         lo, hi = b * cfg.B, min((b + 1) * cfg.B, cfg.N)
         assert max_abs(og[lo:hi], want_o[lo:hi]) <= TOL_BF16
+
+
+@pytest.mark.parametrize("B,d", [(128, 128), (64, 64)])
+def test_maximum_size_lists(B, d):
+    """nb = CALIBATT_MAX_NB = 4096 blocks: a full row (the longest list the kernels stage), an alternating
+    row (the most runs, nb/2), first-and-last blocks, and an empty head; both list forms."""
+    nb = 4096                                   # CALIBATT_MAX_NB
+    N = nb * B - B // 2                         # ragged last block
+    H = 2
+    say(f"[max size] nb={nb} N={N} B={B} d={d}")
+    masks = np.zeros((1, 1, H, nb, nb), np.uint8)
+    masks[0, 0, 0, 0, :] = 1                    # every key block
+    masks[0, 0, 0, 1, ::2] = 1                  # 2048 single-block runs
+    masks[0, 0, 0, nb - 1, [0, nb - 1]] = 1     # first and last block (ragged)
+    # head 1: every list empty
+    q, k, v = random_qkv(H, N, d, "bf16", seed=nb + B)
+    dq, dk, dv = (to_device(x, "bf16") for x in (q, k, v))
+    dm = torch.from_numpy(masks).cuda()
+    sl = cal.compile_skiplist(dm, N, B)
+    il = cal.compile_intervals(dm, N, B)
+    o, lse = alloc_out(H, N, d, "bf16")
+    o_iv, lse_iv = alloc_out(H, N, d, "bf16")
+    scale = float(np.float32(1.0 / np.sqrt(d)))
+    cal.calibatt_block_sparse_attn(dq, dk, dv, o, lse, sl, 0, 0, scale=scale)
+    cal.calibatt_block_sparse_attn_iv(dq, dk, dv, o_iv, lse_iv, il, 0, 0, scale=scale)
+    torch.cuda.synchronize()
+    assert il.n_iv == 1 + nb // 2 + 2
+    assert torch.equal(o.view(torch.int16), o_iv.view(torch.int16))
+    assert torch.equal(lse.view(torch.int32), lse_iv.view(torch.int32))
+    rp, ci, _ = oracle.compile_skiplist(masks)
+    blocks = [0, 1, nb - 1]
+    want_o, want_l = oracle.block_sparse_head(exact_values(q[0], "bf16"), exact_values(k[0], "bf16"),
+                                              exact_values(v[0], "bf16"), rp, ci, 0, B, scale, blocks=blocks)
+    og, lg = host64(o[0]), lse[0].cpu().numpy()
+    for b in blocks:
+        lo, hi = b * B, min((b + 1) * B, N)
+        assert max_abs(og[lo:hi], want_o[lo:hi]) <= TOL_BF16, b
+        assert max_abs(lg[lo:hi], want_l[lo:hi]) <= TOL_LSE_BF16, b
+    # the empty head: O = 0 and lse = -inf everywhere
+    assert torch.all(o[1] == 0)
+    assert torch.all(torch.isneginf(lse[1]))
