@@ -95,6 +95,7 @@ struct SimParams {
   float scale;
   float scale_log2;
   int32_t n_heads;
+  int32_t rows_per_group;   // bf16 path: non-anchor rows per workgroup (set by the launcher)
   int32_t anchors[CALIBATT_MAX_ANCHORS];
   int32_t heads[CALIBATT_MAX_HEADS];
 };

@@ -8,10 +8,13 @@
 // For row r of frame f with nearest anchor a (ties to the smaller anchor):
 //   sim = <P_r, P_a> / (|P_r| |P_a|),  <P_r, P_a> = sum_c sum_j P[(f,r,c)][j] P[(f,a,c)][j],
 // P = softmax over all keys of scale * q . k, normalised with each query's
-// log2-sum-exp from the first (log-sum-exp) pass. One workgroup per
-// (head, frame, row): its waves own 32-column tiles of the row, compute the
-// scores of the row's queries and of the anchor row's queries (the same
-// columns) against one shared K stream, and accumulate the three sums per lane.
+// log2-sum-exp from the first (log-sum-exp) pass. The non-anchor rows of a
+// head, flattened over (frame, row), are split into groups of m whole rows;
+// one workgroup per group gives each lane one (row, column) slot of the group,
+// so m*C fills the waves' 32-lane tiles with few idle lanes whatever C is. All
+// lanes of a workgroup score against one shared K stream, their own row's
+// query and their anchor row's query at the same column, and accumulate the
+// three sums per slot; the rows' totals are then added in column order.
 #include "gfx950_device.h"
 
 namespace calibatt {
@@ -20,7 +23,8 @@ namespace {
 using namespace dev;
 
 constexpr int kPrefetch = 4;
-constexpr int kWaves = 4;
+constexpr int kMaxWaves = 8;
+constexpr int kMaxSlots = kMaxWaves * 32;
 
 // Nearest anchor row of r (ties to the smaller anchor).
 __device__ __forceinline__ int nearest_anchor(const SimParams& p, int r) {
@@ -32,38 +36,46 @@ __device__ __forceinline__ int nearest_anchor(const SimParams& p, int r) {
   return best;
 }
 
+// The i-th non-anchor row (anchors strictly ascending).
+__device__ __forceinline__ int nonanchor_row(const SimParams& p, int i) {
+  int r = i;
+  for (int j = 0; j < p.ka; ++j) r += p.anchors[j] <= r ? 1 : 0;
+  return r;
+}
+
 template <int D>
-__global__ __launch_bounds__(kWaves * 64) void similarity_bf16_kernel(const SimParams p) {
+__global__ __launch_bounds__(kMaxWaves * 64) void similarity_bf16_kernel(const SimParams p) {
   constexpr int SUB = 64;
   constexpr int CPR = D / 8;
   constexpr int KT = SUB / 32;
   constexpr int DS = D / 16;
   constexpr int STAGE = SUB * CPR;
-  constexpr int LPW = STAGE / 64 / kWaves;
-  constexpr int RPI = 64 / CPR;
+  constexpr int NCOP = STAGE / 64;       // 16-byte-per-lane copies per stage
+  constexpr int RPI = 64 / CPR;          // K rows per copy
 
   __shared__ uint4 lds_k[2 * STAGE];
-  __shared__ float red[kWaves][3];
+  __shared__ float part[kMaxSlots][3];   // this pass's per-slot sums
+  __shared__ float rowacc[kMaxSlots][3]; // per-row totals of the group
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int W = __builtin_amdgcn_readfirstlane(blockDim.x >> 6);
   const int h = lane >> 5;
   const int l32 = lane & 31;
   int n_tok = p.N;
   float scale_log2 = p.scale_log2;
   asm volatile("" : "+s"(n_tok), "+s"(scale_log2));
 
+  const int nr = p.R - p.ka;                          // non-anchor rows per frame
+  const int64_t rows_total = (int64_t)p.F * nr;
+  const int m = p.rows_per_group;
+  const int64_t groups = (rows_total + m - 1) / m;
   const int64_t item = xcd_item(blockIdx.x, gridDim.x, 32);
-  const int rows = p.F * p.R;
-  const int head = p.heads[item / rows];
-  const int fr = (int)(item % rows);
-  const int f = fr / p.R, r = fr % p.R;
-  const int a = nearest_anchor(p, r);
-  float* out = p.row_sim + ((int64_t)head * p.F + f) * p.R + r;
-  if (a == r) {                 // an anchor row: similarity with itself
-    if (threadIdx.x == 0) *out = 1.0f;
-    return;
-  }
+  const int head = p.heads[item / groups];
+  const int64_t rho0 = (item % groups) * m;
+  const int mrows = (int)min((int64_t)m, rows_total - rho0);
+  const int slots = mrows * p.C;
+
   const u16* Q = static_cast<const u16*>(p.q) + (int64_t)head * p.head_stride;
   const char* Kb = reinterpret_cast<const char*>(static_cast<const u16*>(p.k) + (int64_t)head * p.head_stride);
   const float* lse = p.lse2 + (int64_t)head * n_tok;
@@ -72,48 +84,54 @@ __global__ __launch_bounds__(kWaves * 64) void similarity_bf16_kernel(const SimP
   const int dpos = lane % CPR;
   const uint32_t dma_lane = (uint32_t)(dq * 2 * D + 16 * (dpos ^ (dq & (CPR - 1))));
   const uint32_t k_lane = (uint32_t)(l32 * 2 * D + 16 * (h ^ (l32 & (CPR - 1))));
-  auto issue = [&](int stage, int i, uint4* dst) {
+  // copy ci of a stage fills K rows [ci*RPI, ci*RPI + RPI) of the stage buffer
+  auto issue = [&](int stage, int ci, uint4* dst) {
     const int row0 = stage * SUB;
-    const int rr = (wave * LPW + i) * RPI;
+    const int rr = ci * RPI;
     const uint32_t off = dma_lane ^ (uint32_t)(16 * (rr & (CPR - 1)));
     if (row0 + SUB <= n_tok) {
-      dma16(Kb + (int64_t)(row0 + rr) * (2 * D), off, dst + (wave * LPW + i) * 64);
+      dma16(Kb + (int64_t)(row0 + rr) * (2 * D), off, dst + ci * 64);
     } else {
       asm volatile("");
       const int b0 = min(row0, n_tok - 1);
       const int grow = min(row0 + rr + dq, n_tok - 1);
-      dma16(Kb + (int64_t)b0 * (2 * D), (uint32_t)((grow - b0) * (2 * D)) + (off & (2 * D - 1)),
-            dst + (wave * LPW + i) * 64);
+      dma16(Kb + (int64_t)b0 * (2 * D), (uint32_t)((grow - b0) * (2 * D)) + (off & (2 * D - 1)), dst + ci * 64);
     }
   };
+  // this wave's copies are ci = wave + n*W, n < my_n
+  const int my_n = wave < NCOP ? (NCOP - wave + W - 1) / W : 0;
 
+  for (int t = threadIdx.x; t < mrows; t += blockDim.x) rowacc[t][0] = rowacc[t][1] = rowacc[t][2] = 0.0f;
   const int n_stages = (n_tok + SUB - 1) / SUB;
-  float dot_t = 0.0f, nr_t = 0.0f, na_t = 0.0f;   // thread 0: totals over column groups
-  for (int c0 = 0; c0 < p.C; c0 += kWaves * 32) {
-    // this wave's 32 columns; columns past C get lse = +inf (probabilities 0)
-    const int c = c0 + wave * 32 + l32;
-    const bool c_ok = c < p.C;
-    const int tr = (f * p.R + r) * p.C + c, ta = (f * p.R + a) * p.C + c;
-    const float lse_r = c_ok ? lse[tr] : INFINITY;
-    const float lse_a = c_ok ? lse[ta] : INFINITY;
+  for (int base = 0; base < slots; base += W * 32) {
+    // this lane's slot: row il of the group, column c; idle slots get lse = +inf
+    const int slot = base + wave * 32 + l32;
+    const bool ok = slot < slots;
+    int tr = 0, ta = 0;
+    if (ok) {
+      const int il = slot / p.C, c = slot % p.C;
+      const int64_t rho = rho0 + il;
+      const int f = (int)(rho / nr);
+      const int r = nonanchor_row(p, (int)(rho % nr));
+      const int a = nearest_anchor(p, r);
+      tr = (f * p.R + r) * p.C + c;
+      ta = (f * p.R + a) * p.C + c;
+    }
+    const float lse_r = ok ? lse[tr] : INFINITY;
+    const float lse_a = ok ? lse[ta] : INFINITY;
     bf16x8 qr[DS], qa[DS];
 #pragma unroll
     for (int s = 0; s < DS; ++s) {
       uint4 x = make_uint4(0, 0, 0, 0), y = make_uint4(0, 0, 0, 0);
-      if (c_ok) {
+      if (ok) {
         x = ld_global16(Q + (int64_t)tr * D + 16 * s + 8 * h);
         y = ld_global16(Q + (int64_t)ta * D + 16 * s + 8 * h);
       }
       qr[s] = bitcast<bf16x8>(x);
       qa[s] = bitcast<bf16x8>(y);
     }
-    if (c0 > 0) {             // the previous group's last stage is done everywhere
-      wait_vmcnt<0>();
-      barrier_no_fence();
-    }
-#pragma unroll
-    for (int i = 0; i < LPW; ++i) issue(0, i, lds_k);
-    float dot = 0.0f, nr = 0.0f, na = 0.0f;
+    for (int n = 0; n < my_n; ++n) issue(0, wave + n * W, lds_k);
+    float dot = 0.0f, nr2 = 0.0f, na2 = 0.0f;
     for (int j = 0; j < n_stages; ++j) {
       const uint4* sk = lds_k + (j & 1) * STAGE;
       uint4* nk = lds_k + ((j + 1) & 1) * STAGE;
@@ -127,7 +145,6 @@ __global__ __launch_bounds__(kWaves * 64) void similarity_bf16_kernel(const SimP
           const char* ptr = reinterpret_cast<const char*>(sk) + 32 * t * (2 * D) + (k_lane ^ (uint32_t)(32 * s));
           return bitcast<bf16x8>(*reinterpret_cast<const uint4*>(ptr));
         };
-        constexpr int kEvery = (KT * DS) / LPW > 0 ? (KT * DS) / LPW : 1;
         bf16x8 ring[kPrefetch];
 #pragma unroll
         for (int i = 0; i < kPrefetch; ++i) ring[i] = read_k(i);
@@ -138,12 +155,12 @@ __global__ __launch_bounds__(kWaves * 64) void similarity_bf16_kernel(const SimP
           if (idx + kPrefetch < KT * DS) ring[idx % kPrefetch] = read_k(idx + kPrefetch);
           sr[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qr[s], s == 0 ? f32x16{} : sr[t], 0, 0, 0);
           sa[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qa[s], s == 0 ? f32x16{} : sa[t], 0, 0, 0);
-          if (has_next && idx % kEvery == kEvery - 1 && idx / kEvery < LPW) issue(j + 1, idx / kEvery, nk);
+          // the next stage's copies go between the MFMAs, one every second step
+          if (has_next && (idx & 1) && (idx >> 1) < my_n) issue(j + 1, wave + (idx >> 1) * W, nk);
           __builtin_amdgcn_sched_barrier(0);
         }
         if (has_next) {
-#pragma unroll
-          for (int i = (KT * DS) / kEvery; i < LPW; ++i) issue(j + 1, i, nk);
+          for (int n = (KT * DS) / 2; n < my_n; ++n) issue(j + 1, wave + n * W, nk);
         }
       }
       const int valid = n_tok - j * SUB;
@@ -168,32 +185,52 @@ __global__ __launch_bounds__(kWaves * 64) void similarity_bf16_kernel(const SimP
           const float pr = __builtin_amdgcn_exp2f(__builtin_fmaf(sr[t][e], scale_log2, -lse_r));
           const float pa = __builtin_amdgcn_exp2f(__builtin_fmaf(sa[t][e], scale_log2, -lse_a));
           dot = __builtin_fmaf(pr, pa, dot);
-          nr = __builtin_fmaf(pr, pr, nr);
-          na = __builtin_fmaf(pa, pa, na);
+          nr2 = __builtin_fmaf(pr, pr, nr2);
+          na2 = __builtin_fmaf(pa, pa, na2);
         }
     }
-    // sum the wave's 64 lanes (both key halves of 32 columns), then the waves, in a fixed order
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1) {
-      dot += __shfl_xor(dot, off);
-      nr += __shfl_xor(nr, off);
-      na += __shfl_xor(na, off);
-    }
-    if (lane == 0) {
-      red[wave][0] = dot;
-      red[wave][1] = nr;
-      red[wave][2] = na;
+    // the two key halves of a slot sit in lanes l32 and l32 + 32
+    dot += __shfl_xor(dot, 32);
+    nr2 += __shfl_xor(nr2, 32);
+    na2 += __shfl_xor(na2, 32);
+    if (h == 0) {
+      part[wave * 32 + l32][0] = dot;
+      part[wave * 32 + l32][1] = nr2;
+      part[wave * 32 + l32][2] = na2;
     }
     __syncthreads();
-    if (threadIdx.x == 0) {
-      for (int w = 0; w < kWaves; ++w) {
-        dot_t += red[w][0];
-        nr_t += red[w][1];
-        na_t += red[w][2];
+    // rows touched by this pass add their slots in column order
+    const int end = min(base + W * 32, slots);
+    const int il0 = base / p.C, il1 = (end - 1) / p.C;
+    for (int t = il0 + (int)threadIdx.x; t <= il1; t += blockDim.x) {
+      const int s0 = max(t * p.C, base), s1 = min((t + 1) * p.C, end);
+      float sd = 0.0f, sn = 0.0f, sa2 = 0.0f;
+      for (int q = s0; q < s1; ++q) {
+        sd += part[q - base][0];
+        sn += part[q - base][1];
+        sa2 += part[q - base][2];
       }
+      rowacc[t][0] += sd;
+      rowacc[t][1] += sn;
+      rowacc[t][2] += sa2;
     }
+    __syncthreads();   // part[] and the K buffers are reused by the next pass
   }
-  if (threadIdx.x == 0) *out = dot_t / sqrtf(nr_t * na_t);
+  for (int t = threadIdx.x; t < mrows; t += blockDim.x) {
+    const int64_t rho = rho0 + t;
+    const int f = (int)(rho / nr);
+    const int r = nonanchor_row(p, (int)(rho % nr));
+    p.row_sim[((int64_t)head * p.F + f) * p.R + r] = rowacc[t][0] / sqrtf(rowacc[t][1] * rowacc[t][2]);
+  }
+}
+
+// Anchor rows compare with themselves: similarity 1.
+__global__ void anchor_ones_kernel(const SimParams p) {
+  const int head = p.heads[blockIdx.x];
+  for (int i = threadIdx.x; i < p.F * p.ka; i += blockDim.x) {
+    const int f = i / p.ka, j = i % p.ka;
+    p.row_sim[((int64_t)head * p.F + f) * p.R + p.anchors[j]] = 1.0f;
+  }
 }
 
 // fp32 inputs: one thread per column of the row pair, K tiles in LDS.
@@ -286,18 +323,47 @@ __global__ void flags_kernel(const float* __restrict__ sims, int P, int H, int F
 
 }  // namespace
 
+// Rows per workgroup and waves for rows of C columns (bf16 path): the largest
+// product of the busy fraction of the m*C slots and the fraction of a CU's
+// wave slots (two waves per SIMD at this kernel's register use) the resident
+// workgroups fill; ties go to more waves (a K stream shared more widely).
+// Rows wider than the largest workgroup take one row per group, in passes.
+static void pick_group(int C, int& m, int& W) {
+  if (C > kMaxSlots) {
+    m = 1;
+    W = kMaxWaves;
+    return;
+  }
+  double best = -1.0;
+  for (int mm = 1; mm * C <= kMaxSlots; ++mm) {
+    const int w = (mm * C + 31) / 32;
+    const double score = (double)(mm * C) / (32.0 * w) * (double)((kMaxWaves / w) * w) / kMaxWaves;
+    if (score > best + 1e-9 || (score > best - 1e-9 && w > W)) {
+      best = score;
+      m = mm;
+      W = w;
+    }
+  }
+}
+
 hipError_t launch_similarity(const SimParams& p, int d, bool f32, hipStream_t s) {
-  const int64_t items = (int64_t)p.n_heads * p.F * p.R;
-  if (items == 0) return hipSuccess;
+  if (p.n_heads == 0) return hipSuccess;
   if (f32) {
+    const int64_t items = (int64_t)p.n_heads * p.F * p.R;
     if (d == 128) hipLaunchKernelGGL(similarity_f32_kernel<128>, dim3((unsigned)items), dim3(64), 0, s, p);
     else if (d == 64) hipLaunchKernelGGL(similarity_f32_kernel<64>, dim3((unsigned)items), dim3(64), 0, s, p);
     else return hipErrorInvalidValue;
-  } else {
-    if (d == 128) hipLaunchKernelGGL(similarity_bf16_kernel<128>, dim3((unsigned)items), dim3(kWaves * 64), 0, s, p);
-    else if (d == 64) hipLaunchKernelGGL(similarity_bf16_kernel<64>, dim3((unsigned)items), dim3(kWaves * 64), 0, s, p);
-    else return hipErrorInvalidValue;
+    return hipGetLastError();
   }
+  SimParams q = p;
+  int W = 0;
+  pick_group(p.C, q.rows_per_group, W);
+  const int64_t rows = (int64_t)p.F * (p.R - p.ka);
+  const int64_t items = (int64_t)p.n_heads * ((rows + q.rows_per_group - 1) / q.rows_per_group);
+  if (d == 128) hipLaunchKernelGGL(similarity_bf16_kernel<128>, dim3((unsigned)items), dim3(W * 64), 0, s, q);
+  else if (d == 64) hipLaunchKernelGGL(similarity_bf16_kernel<64>, dim3((unsigned)items), dim3(W * 64), 0, s, q);
+  else return hipErrorInvalidValue;
+  hipLaunchKernelGGL(anchor_ones_kernel, dim3((unsigned)p.n_heads), dim3(64), 0, s, q);
   return hipGetLastError();
 }
 

@@ -33,6 +33,10 @@ def _sims(q, k, F, R, C, anchors, dtype, scale=None):
 @pytest.mark.parametrize("F,R,C,anchors,d,dtype", [
     (2, 10, 20, [2, 7], 128, "bf16"), (3, 16, 16, [4, 12], 64, "bf16"), (2, 30, 8, [3, 9, 15, 21, 27], 128, "bf16"),
     (1, 5, 150, [2], 128, "bf16"), (2, 8, 10, [1, 5], 64, "f32"), (2, 6, 5, [0], 128, "f32"),
+    # rows wider than one workgroup (two passes), the 480p row width with a short last group,
+    # one column per row (hundreds of rows per group, fewer keys than one stage), an odd width
+    (1, 3, 300, [1], 64, "bf16"), (2, 4, 52, [1], 128, "bf16"), (2, 7, 1, [3], 64, "bf16"),
+    (3, 5, 33, [0, 4], 128, "bf16"),
 ])
 def test_row_similarity_small(F, R, C, anchors, d, dtype):
     say(f"[repetition] F={F} R={R} C={C} anchors={anchors} d={d} {dtype}")
@@ -46,6 +50,25 @@ def test_row_similarity_small(F, R, C, anchors, d, dtype):
         err = float(np.max(np.abs(got[h] - want)))
         say(f"  head {h}: max|d sim| = {err:.2e}, sims in [{want.min():.3f}, {want.max():.3f}]")
         assert err <= TOL_SIM, (h, err)
+
+
+def test_head_subset_leaves_other_heads():
+    F, R, C, d, H = 2, 6, 24, 128, 3
+    N = F * R * C
+    anchors = [1, 4]
+    q, k = workloads.make_calibration_prompts(N, d, F, R, C, H, 1, seed=9300)
+    q, k = q[0], k[0]
+    scale = float(np.float32(1.0 / np.sqrt(d)))
+    lse = torch.full((H, N), float("nan"), dtype=torch.float32, device="cuda")
+    sim = torch.full((H, F, R), float("nan"), dtype=torch.float32, device="cuda")
+    cal.calibatt_spatial_similarity(to_device(q, "bf16"), to_device(k, "bf16"), F, R, C, anchors, lse, sim,
+                                    heads=[2, 0], scale=scale)
+    torch.cuda.synchronize()
+    got = sim.cpu().numpy().astype(np.float64)
+    assert np.all(np.isnan(got[1]))
+    for h in (0, 2):
+        want = oracle.row_similarity(exact_values(q[h], "bf16"), exact_values(k[h], "bf16"), F, R, C, anchors, scale)
+        assert float(np.max(np.abs(got[h] - want))) <= TOL_SIM
 
 
 def test_identical_rows_give_one():
