@@ -295,9 +295,8 @@ def calibration_bench(args):
     keep_ms = a.elapsed_time(b)
     # spatial-repetition branch: per prompt, row similarities of all heads; then the flags
     anchors = workloads.equally_spaced_anchor_rows(cfg.R, cfg.n_anchor)
-    lse_work = torch.empty((H, N), dtype=torch.float32, device=dev)
     sims = torch.empty((args.prompts, H, cfg.F, cfg.R), dtype=torch.float32, device=dev)
-    cal.calibatt_spatial_similarity(qd, kd, cfg.F, cfg.R, cfg.C, anchors, lse_work, sims[0], stream=stream)
+    cal.calibatt_spatial_similarity(qd, kd, cfg.F, cfg.R, cfg.C, anchors, sims[0], stream=stream)
     torch.cuda.synchronize()
     sim_ms, simk_ms = [], []
     for p in range(args.prompts):
@@ -306,7 +305,7 @@ def calibration_bench(args):
         b.record(stream)
         c.record(stream)
         cal.calibatt_set_kernel_events(b.cuda_event, c.cuda_event)
-        cal.calibatt_spatial_similarity(qd, kd, cfg.F, cfg.R, cfg.C, anchors, lse_work, sims[p], stream=stream)
+        cal.calibatt_spatial_similarity(qd, kd, cfg.F, cfg.R, cfg.C, anchors, sims[p], stream=stream)
         e.record(stream)
         torch.cuda.synchronize()
         sim_ms.append(a.elapsed_time(e))

@@ -88,7 +88,7 @@ def _load():
     lib.calibatt_keep_frequency.argtypes = [vp, i64, i32, f32, vp, vp]
     lib.calibatt_keep_frequency.restype = i32
     lib.calibatt_spatial_similarity.argtypes = [vp, vp, i32, i32, i32, i32, f32, i32, i32, i32, vp, i32, vp, vp,
-                                                vp, i32, vp]
+                                                i32, vp]
     lib.calibatt_spatial_similarity.restype = i32
     lib.calibatt_repetition_flags.argtypes = [vp, i32, i32, i32, i32, vp, i32, f32, vp, vp, vp]
     lib.calibatt_repetition_flags.restype = i32
@@ -328,15 +328,15 @@ def calibatt_keep_frequency(counts, n_prompts: int, rho: float, mask, stream=Non
                                        _stream(stream)))
 
 
-def calibatt_spatial_similarity(q, k, F: int, R: int, C: int, anchor_rows, lse_work, row_sim, heads=None,
+def calibatt_spatial_similarity(q, k, F: int, R: int, C: int, anchor_rows, row_sim, heads=None,
                                 scale: float | None = None, stream=None) -> None:
-    """Row similarities [H, F, R] (float32 device tensor) of one prompt; lse_work: float32 [H, N] workspace."""
+    """Row similarities [H, F, R] (float32 device tensor) of one prompt."""
     H, N, d = q.shape
     scale = float(np.float32(1.0 / np.sqrt(d))) if scale is None else scale
     aarr, ka = _host_i32(anchor_rows)
     harr, nh = _host_i32(heads)
     _check(lib.calibatt_spatial_similarity(_ptr(q), _ptr(k), H, N, d, _dtype_code(q), scale, F, R, C,
-                                           aarr.ctypes.data, ka, _ptr(lse_work), _ptr(row_sim),
+                                           aarr.ctypes.data, ka, _ptr(row_sim),
                                            harr.ctypes.data if harr is not None else None, nh, _stream(stream)))
 
 

@@ -442,39 +442,19 @@ calibatt_status_t calibatt_keep_frequency(const int32_t* counts, int64_t n, int3
 
 calibatt_status_t calibatt_spatial_similarity(const void* q, const void* k, int32_t H, int32_t N, int32_t d,
                                               calibatt_dtype_t dtype, float scale, int32_t F, int32_t R, int32_t C,
-                                              const int32_t* anchor_rows, int32_t k_anchors, float* lse_work,
-                                              float* row_sim, const int32_t* heads, int32_t n_heads, void* stream) {
+                                              const int32_t* anchor_rows, int32_t k_anchors, float* row_sim,
+                                              const int32_t* heads, int32_t n_heads, void* stream) {
   calibatt_status_t st = check_tensors(q, k, q, row_sim, H, N, d, dtype, scale);
   if (st != CALIBATT_OK) return st;
-  if (!lse_work) return fail(CALIBATT_ERR_INVALID_ARG, "lse_work is NULL");
   if ((st = check_anchors(N, F, R, C, anchor_rows, k_anchors)) != CALIBATT_OK) return st;
   if (k_anchors >= R) return fail(CALIBATT_ERR_INVALID_ARG, "every row is an anchor row (k = R): nothing to compare");
-  if (ceil_div(N, 128) > CALIBATT_MAX_NB) return fail(CALIBATT_ERR_INVALID_ARG, "N too large");
   std::vector<int32_t> hs;
   if ((st = check_heads(heads, n_heads, H, hs)) != CALIBATT_OK) return st;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  // 1. each query's log2-sum-exp over all keys
-  calibatt::EnergyParams e;
-  std::memset(&e, 0, sizeof(e));
-  e.q = q;
-  e.k = k;
-  e.lse2 = lse_work;
-  e.head_stride = (int64_t)N * d;
-  e.N = N;
-  e.nb = (int32_t)ceil_div(N, 128);
-  e.scale = scale;
-  e.scale_log2 = scale * 1.4426950408889634f;
-  e.dtype_f32 = dtype == CALIBATT_F32 ? 1 : 0;
-  e.n_heads = (int32_t)hs.size();
-  for (size_t i = 0; i < hs.size(); ++i) e.heads[i] = hs[i];
-  hipError_t err = calibatt::launch_row_lse(e, d, s);
-  if (err != hipSuccess) return hip_fail(err, "log-sum-exp kernel launch");
-  // 2. row against nearest anchor row
   calibatt::SimParams p;
   std::memset(&p, 0, sizeof(p));
   p.q = q;
   p.k = k;
-  p.lse2 = lse_work;
   p.row_sim = row_sim;
   p.head_stride = (int64_t)N * d;
   p.N = N;
@@ -484,11 +464,12 @@ calibatt_status_t calibatt_spatial_similarity(const void* q, const void* k, int3
   p.ka = k_anchors;
   for (int32_t i = 0; i < k_anchors; ++i) p.anchors[i] = anchor_rows[i];
   p.scale = scale;
-  p.scale_log2 = e.scale_log2;
-  p.n_heads = e.n_heads;
+  p.scale_log2 = scale * 1.4426950408889634f;
+  p.n_heads = (int32_t)hs.size();
   for (size_t i = 0; i < hs.size(); ++i) p.heads[i] = hs[i];
   hipEvent_t eb = g_ev_begin, ee = g_ev_end;
   g_ev_begin = g_ev_end = nullptr;
+  hipError_t err;
   if (eb && (err = hipEventRecord(eb, s)) != hipSuccess) return hip_fail(err, "hipEventRecord");
   if ((err = calibatt::launch_similarity(p, d, dtype == CALIBATT_F32, s)) != hipSuccess)
     return hip_fail(err, "similarity kernel launch");

@@ -38,9 +38,7 @@ constexpr int kPrefetch = 4;            // K operand reads in flight ahead of th
 // column and half of the 64 keys of a stage); K moves HBM -> LDS by DMA,
 // double-buffered per 64-key stage, the next stage issued between the MFMAs.
 // ---------------------------------------------------------------------------
-// LSE_ONLY: run the first pass alone and store each query's log2-sum-exp
-// (of scale * q . k over all keys) in p.lse2 instead of computing energies.
-template <int D, int BLK, bool LSE_ONLY>
+template <int D, int BLK>
 __global__ __launch_bounds__(BLK * 2) void energy_bf16_kernel(const EnergyParams p) {
   constexpr int NW = BLK / 32;
   constexpr int SUB = 64;
@@ -108,7 +106,7 @@ __global__ __launch_bounds__(BLK * 2) void energy_bf16_kernel(const EnergyParams
   float m_run = -INFINITY, l_run = 0.0f, lse2 = 0.0f;
   float e_acc = 0.0f;
 
-  for (int pass = 0; pass < (LSE_ONLY ? 1 : 2); ++pass) {
+  for (int pass = 0; pass < 2; ++pass) {
     if (pass == 1) {
       // every wave is done with the last stage of the first pass before stage 0 is copied again
       wait_vmcnt<0>();
@@ -211,10 +209,6 @@ __global__ __launch_bounds__(BLK * 2) void energy_bf16_kernel(const EnergyParams
       const float L = l_run * __builtin_amdgcn_exp2f(m_run - M) + l_o * __builtin_amdgcn_exp2f(m_o - M);
       // queries past N get +inf, so every probability of theirs is exactly 0
       lse2 = q_ok ? M + __log2f(L) : INFINITY;
-      if (LSE_ONLY) {
-        if (q_ok && h == 0) p.lse2[(int64_t)head * n_tok + qtok] = lse2;
-        return;
-      }
     }
   }
 
@@ -232,7 +226,7 @@ __global__ __launch_bounds__(BLK * 2) void energy_bf16_kernel(const EnergyParams
 
 // fp32 energies: one thread per query, K tiles in LDS read as broadcasts,
 // fp32 FMA and expf; the same two passes.
-template <int D, int BLK, bool LSE_ONLY>
+template <int D, int BLK>
 __global__ __launch_bounds__(BLK) void energy_f32_kernel(const EnergyParams p) {
   extern __shared__ float smem[];
   float* ks = smem;                      // [BLK][D]
@@ -248,7 +242,7 @@ __global__ __launch_bounds__(BLK) void energy_f32_kernel(const EnergyParams p) {
 #pragma unroll
   for (int i = 0; i < D; ++i) q[i] = q_ok ? Q[(int64_t)qtok * D + i] : 0.0f;
   float m = -INFINITY, l = 0.0f, lse = 0.0f;
-  for (int pass = 0; pass < (LSE_ONLY ? 1 : 2); ++pass) {
+  for (int pass = 0; pass < 2; ++pass) {
     for (int c = 0; c < nb; ++c) {
       const int nk = min(BLK, p.N - c * BLK);
       __syncthreads();
@@ -283,8 +277,6 @@ __global__ __launch_bounds__(BLK) void energy_f32_kernel(const EnergyParams p) {
     }
     if (pass == 0) lse = m + logf(l);
   }
-  // log2-sum-exp of scale * q . k (the bf16 kernel's unit)
-  if (LSE_ONLY && q_ok) p.lse2[(int64_t)head * p.N + qtok] = lse * 1.4426950408889634f;
 }
 
 // ---------------------------------------------------------------------------
@@ -362,20 +354,20 @@ __global__ void keep_kernel(const int32_t* __restrict__ counts, int64_t n, int32
     out[i] = counts[i] >= k_min ? 1 : 0;
 }
 
-template <int D, int BLK, bool LSE_ONLY>
+template <int D, int BLK>
 hipError_t launch_energy_typed(const EnergyParams& p, hipStream_t s) {
   const int64_t items = (int64_t)p.n_heads * p.nb;
   if (items == 0) return hipSuccess;
   if (p.dtype_f32) {
     const size_t smem = (size_t)(BLK * D + BLK) * sizeof(float);
-    auto kern = energy_f32_kernel<D, BLK, LSE_ONLY>;
+    auto kern = energy_f32_kernel<D, BLK>;
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(kern, dim3((unsigned)items), dim3(BLK), smem, s, p);
   } else {
     const size_t smem = (size_t)(BLK / 32) * p.nb * sizeof(float);
-    auto kern = energy_bf16_kernel<D, BLK, LSE_ONLY>;
+    auto kern = energy_bf16_kernel<D, BLK>;
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
     if (e != hipSuccess) return e;
@@ -387,16 +379,10 @@ hipError_t launch_energy_typed(const EnergyParams& p, hipStream_t s) {
 }  // namespace
 
 hipError_t launch_energy(const EnergyParams& p, int d, int blk, hipStream_t s) {
-  if (d == 128 && blk == 128) return launch_energy_typed<128, 128, false>(p, s);
-  if (d == 64 && blk == 128) return launch_energy_typed<64, 128, false>(p, s);
-  if (d == 128 && blk == 64) return launch_energy_typed<128, 64, false>(p, s);
-  if (d == 64 && blk == 64) return launch_energy_typed<64, 64, false>(p, s);
-  return hipErrorInvalidValue;
-}
-
-hipError_t launch_row_lse(const EnergyParams& p, int d, hipStream_t s) {
-  if (d == 128) return launch_energy_typed<128, 128, true>(p, s);
-  if (d == 64) return launch_energy_typed<64, 128, true>(p, s);
+  if (d == 128 && blk == 128) return launch_energy_typed<128, 128>(p, s);
+  if (d == 64 && blk == 128) return launch_energy_typed<64, 128>(p, s);
+  if (d == 128 && blk == 64) return launch_energy_typed<128, 64>(p, s);
+  if (d == 64 && blk == 64) return launch_energy_typed<64, 64>(p, s);
   return hipErrorInvalidValue;
 }
 

@@ -71,7 +71,6 @@ struct EnergyParams {
   const void* q;
   const void* k;
   float* energy;            // [H][nb][nb]
-  float* lse2;              // [H][N] log2-sum-exp per query (log-sum-exp pass only)
   int64_t head_stride;      // N * d elements
   int32_t N;
   int32_t nb;
@@ -82,12 +81,11 @@ struct EnergyParams {
   int32_t heads[CALIBATT_MAX_HEADS];
 };
 
-// Spatial-row similarities of selected heads for one prompt: one work item
-// per (head, frame, spatial row).
+// Spatial-row similarities of selected heads for one prompt, in one pass over
+// the keys (each query's softmax normaliser is accumulated alongside).
 struct SimParams {
   const void* q;
   const void* k;
-  const float* lse2;        // [H][N] log2-sum-exp per query (from launch_row_lse)
   float* row_sim;           // [H][F][R]
   int64_t head_stride;      // N * d elements
   int32_t N;
@@ -115,7 +113,6 @@ hipError_t launch_attn_bf16(const AttnParams& p, int d, int blk, hipStream_t s);
 hipError_t launch_attn_f32(const AttnParams& p, int d, int blk, hipStream_t s);
 hipError_t launch_broadcast(const BcastParams& p, hipStream_t s);
 hipError_t launch_energy(const EnergyParams& p, int d, int blk, hipStream_t s);
-hipError_t launch_row_lse(const EnergyParams& p, int d, hipStream_t s);   // 128-query tiles
 hipError_t launch_similarity(const SimParams& p, int d, bool f32, hipStream_t s);
 hipError_t launch_rep_flags(const float* sims, int P, int H, int F, int R, const RepFlagParams& q, uint8_t* flags,
                             float* mean, hipStream_t s);

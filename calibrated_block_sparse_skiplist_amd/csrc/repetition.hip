@@ -7,8 +7,12 @@
 //
 // For row r of frame f with nearest anchor a (ties to the smaller anchor):
 //   sim = <P_r, P_a> / (|P_r| |P_a|),  <P_r, P_a> = sum_c sum_j P[(f,r,c)][j] P[(f,a,c)][j],
-// P = softmax over all keys of scale * q . k, normalised with each query's
-// log2-sum-exp from the first (log-sum-exp) pass. The non-anchor rows of a
+// P = softmax over all keys of scale * q . k. One pass over the keys: a slot
+// keeps, relative to a reference maximum per query, the sums
+//   l_r = sum e_r, l_a = sum e_a, D = sum e_r e_a, A = sum e_r^2, B = sum e_a^2
+// (e = exp2(scale_log2 * s - m)); its column then contributes D / (l_r l_a),
+// A / l_r^2 and B / l_a^2, which are the sums over the normalised
+// probabilities. The non-anchor rows of a
 // head, flattened over (frame, row), are split into groups of m whole rows;
 // one workgroup per group gives each lane one (row, column) slot of the group,
 // so m*C fills the waves' 32-lane tiles with few idle lanes whatever C is. All
@@ -24,6 +28,9 @@ using namespace dev;
 
 constexpr int kPrefetch = 4;
 constexpr int kMaxWaves = 8;
+// A reference maximum moves only when a stage's scores pass it by more than
+// this (log2 units), so e <= 2^8 and the squared sums stay far from overflow.
+constexpr float kRescaleThreshold = 8.0f;
 constexpr int kMaxSlots = kMaxWaves * 32;
 
 // Nearest anchor row of r (ties to the smaller anchor).
@@ -78,8 +85,6 @@ __global__ __launch_bounds__(kMaxWaves * 64) void similarity_bf16_kernel(const S
 
   const u16* Q = static_cast<const u16*>(p.q) + (int64_t)head * p.head_stride;
   const char* Kb = reinterpret_cast<const char*>(static_cast<const u16*>(p.k) + (int64_t)head * p.head_stride);
-  const float* lse = p.lse2 + (int64_t)head * n_tok;
-
   const int dq = lane / CPR;
   const int dpos = lane % CPR;
   const uint32_t dma_lane = (uint32_t)(dq * 2 * D + 16 * (dpos ^ (dq & (CPR - 1))));
@@ -104,7 +109,7 @@ __global__ __launch_bounds__(kMaxWaves * 64) void similarity_bf16_kernel(const S
   for (int t = threadIdx.x; t < mrows; t += blockDim.x) rowacc[t][0] = rowacc[t][1] = rowacc[t][2] = 0.0f;
   const int n_stages = (n_tok + SUB - 1) / SUB;
   for (int base = 0; base < slots; base += W * 32) {
-    // this lane's slot: row il of the group, column c; idle slots get lse = +inf
+    // this lane's slot: row il of the group, column c (idle slots score q = 0; their sums are never read)
     const int slot = base + wave * 32 + l32;
     const bool ok = slot < slots;
     int tr = 0, ta = 0;
@@ -117,8 +122,6 @@ __global__ __launch_bounds__(kMaxWaves * 64) void similarity_bf16_kernel(const S
       tr = (f * p.R + r) * p.C + c;
       ta = (f * p.R + a) * p.C + c;
     }
-    const float lse_r = ok ? lse[tr] : INFINITY;
-    const float lse_a = ok ? lse[ta] : INFINITY;
     bf16x8 qr[DS], qa[DS];
 #pragma unroll
     for (int s = 0; s < DS; ++s) {
@@ -131,7 +134,9 @@ __global__ __launch_bounds__(kMaxWaves * 64) void similarity_bf16_kernel(const S
       qa[s] = bitcast<bf16x8>(y);
     }
     for (int n = 0; n < my_n; ++n) issue(0, wave + n * W, lds_k);
-    float dot = 0.0f, nr2 = 0.0f, na2 = 0.0f;
+    // the reference maxima are shared by a slot's two key halves (lanes l32, l32 + 32)
+    float m_r = -INFINITY, m_a = -INFINITY;
+    float l_r = 0.0f, l_a = 0.0f, dot = 0.0f, nr2 = 0.0f, na2 = 0.0f;
     for (int j = 0; j < n_stages; ++j) {
       const uint4* sk = lds_k + (j & 1) * STAGE;
       uint4* nk = lds_k + ((j + 1) & 1) * STAGE;
@@ -178,21 +183,60 @@ __global__ __launch_bounds__(kMaxWaves * 64) void similarity_bf16_kernel(const S
             }
           }
       }
+      float xr = -INFINITY, xa = -INFINITY;
 #pragma unroll
       for (int t = 0; t < KT; ++t)
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
-          const float pr = __builtin_amdgcn_exp2f(__builtin_fmaf(sr[t][e], scale_log2, -lse_r));
-          const float pa = __builtin_amdgcn_exp2f(__builtin_fmaf(sa[t][e], scale_log2, -lse_a));
-          dot = __builtin_fmaf(pr, pa, dot);
-          nr2 = __builtin_fmaf(pr, pr, nr2);
-          na2 = __builtin_fmaf(pa, pa, na2);
+          xr = fmaxf(xr, sr[t][e]);
+          xa = fmaxf(xa, sa[t][e]);
         }
+      const float br = xr * scale_log2, ba = xa * scale_log2;
+      if (__ballot(br > m_r + kRescaleThreshold || ba > m_a + kRescaleThreshold) != 0) {
+        asm volatile("");   // rare: keep it a branch
+        const float nm_r = fmaxf(m_r, fmaxf(br, __shfl_xor(br, 32)));
+        const float nm_a = fmaxf(m_a, fmaxf(ba, __shfl_xor(ba, 32)));
+        const float fr = __builtin_amdgcn_exp2f(m_r - nm_r);   // 0 while m is -inf
+        const float fa = __builtin_amdgcn_exp2f(m_a - nm_a);
+        l_r *= fr;
+        l_a *= fa;
+        dot *= fr * fa;
+        nr2 *= fr * fr;
+        na2 *= fa * fa;
+        m_r = nm_r;
+        m_a = nm_a;
+      }
+      // the stage's terms are summed apart and then added to the totals: one
+      // fp32 chain over all of a lane's keys would lose ~sqrt(N/2) ulps
+      float s_lr = 0.0f, s_la = 0.0f, s_d = 0.0f, s_nr = 0.0f, s_na = 0.0f;
+#pragma unroll
+      for (int t = 0; t < KT; ++t)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const float er = __builtin_amdgcn_exp2f(__builtin_fmaf(sr[t][e], scale_log2, -m_r));
+          const float ea = __builtin_amdgcn_exp2f(__builtin_fmaf(sa[t][e], scale_log2, -m_a));
+          s_lr += er;
+          s_la += ea;
+          s_d = __builtin_fmaf(er, ea, s_d);
+          s_nr = __builtin_fmaf(er, er, s_nr);
+          s_na = __builtin_fmaf(ea, ea, s_na);
+        }
+      l_r += s_lr;
+      l_a += s_la;
+      dot += s_d;
+      nr2 += s_nr;
+      na2 += s_na;
     }
-    // the two key halves of a slot sit in lanes l32 and l32 + 32
+    // the two key halves of a slot sit in lanes l32 and l32 + 32 (same reference maxima)
+    l_r += __shfl_xor(l_r, 32);
+    l_a += __shfl_xor(l_a, 32);
     dot += __shfl_xor(dot, 32);
     nr2 += __shfl_xor(nr2, 32);
     na2 += __shfl_xor(na2, 32);
+    // the column's sums over normalised probabilities
+    dot = dot / (l_r * l_a);
+    nr2 = nr2 / (l_r * l_r);
+    na2 = na2 / (l_a * l_a);
     if (h == 0) {
       part[wave * 32 + l32][0] = dot;
       part[wave * 32 + l32][1] = nr2;
@@ -233,7 +277,8 @@ __global__ void anchor_ones_kernel(const SimParams p) {
   }
 }
 
-// fp32 inputs: one thread per column of the row pair, K tiles in LDS.
+// fp32 inputs: one thread per column of the row pair, K tiles in LDS; the
+// same one-pass sums with an exact running maximum (natural exponent).
 template <int D>
 __global__ __launch_bounds__(64) void similarity_f32_kernel(const SimParams p) {
   constexpr int T = 64;                  // keys per LDS tile, columns per pass
@@ -251,8 +296,6 @@ __global__ __launch_bounds__(64) void similarity_f32_kernel(const SimParams p) {
   }
   const float* Q = static_cast<const float*>(p.q) + (int64_t)head * p.head_stride;
   const float* K = static_cast<const float*>(p.k) + (int64_t)head * p.head_stride;
-  const float* lse = p.lse2 + (int64_t)head * p.N;
-  const float ln2 = 0.6931471805599453f;
   float dot_t = 0.0f, nr_t = 0.0f, na_t = 0.0f;
   for (int c0 = 0; c0 < p.C; c0 += T) {
     const int c = c0 + threadIdx.x;
@@ -264,7 +307,7 @@ __global__ __launch_bounds__(64) void similarity_f32_kernel(const SimParams p) {
       qr[i] = ok ? Q[(int64_t)tr * D + i] : 0.0f;
       qa[i] = ok ? Q[(int64_t)ta * D + i] : 0.0f;
     }
-    const float lr = ok ? lse[tr] * ln2 : INFINITY, la = ok ? lse[ta] * ln2 : INFINITY;
+    float m_r = -INFINITY, m_a = -INFINITY, l_r = 0.0f, l_a = 0.0f;
     float dot = 0.0f, nr = 0.0f, na = 0.0f;
     for (int k0 = 0; k0 < p.N; k0 += T) {
       const int nk = min(T, p.N - k0);
@@ -278,15 +321,32 @@ __global__ __launch_bounds__(64) void similarity_f32_kernel(const SimParams p) {
           sr = __builtin_fmaf(qr[i], ks[j * D + i], sr);
           sa = __builtin_fmaf(qa[i], ks[j * D + i], sa);
         }
-        const float pr = expf(sr * p.scale - lr), pa = expf(sa * p.scale - la);
-        dot = __builtin_fmaf(pr, pa, dot);
-        nr = __builtin_fmaf(pr, pr, nr);
-        na = __builtin_fmaf(pa, pa, na);
+        const float xr = sr * p.scale, xa = sa * p.scale;
+        if (xr > m_r) {
+          const float g = expf(m_r - xr);
+          l_r *= g;
+          dot *= g;
+          nr *= g * g;
+          m_r = xr;
+        }
+        if (xa > m_a) {
+          const float g = expf(m_a - xa);
+          l_a *= g;
+          dot *= g;
+          na *= g * g;
+          m_a = xa;
+        }
+        const float er = expf(xr - m_r), ea = expf(xa - m_a);
+        l_r += er;
+        l_a += ea;
+        dot = __builtin_fmaf(er, ea, dot);
+        nr = __builtin_fmaf(er, er, nr);
+        na = __builtin_fmaf(ea, ea, na);
       }
     }
-    red[threadIdx.x][0] = dot;
-    red[threadIdx.x][1] = nr;
-    red[threadIdx.x][2] = na;
+    red[threadIdx.x][0] = ok ? dot / (l_r * l_a) : 0.0f;
+    red[threadIdx.x][1] = ok ? nr / (l_r * l_r) : 0.0f;
+    red[threadIdx.x][2] = ok ? na / (l_a * l_a) : 0.0f;
     __syncthreads();
     if (threadIdx.x == 0) {
       for (int t = 0; t < T; ++t) {

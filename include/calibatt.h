@@ -276,20 +276,19 @@ calibatt_status_t calibatt_keep_frequency(const int32_t* counts, int64_t n, int3
  *   row_sim[h][f][r] = <P_r, P_a> / (|P_r| |P_a|),
  *   <P_r, P_a> = sum_{c < C} sum_{j < N} P[(f*R + r)*C + c][j] * P[(f*R + a)*C + c][j],
  * P = softmax over all N keys of scale * Q[h][i] . K[h][j]; anchor rows get 1.
+ * One pass over the keys: each query's softmax normaliser is accumulated with
+ * the sums, so no workspace is needed.
  *   q, k        [H][N][d] (bf16 or fp32), device, read-only; N = F*R*C.
  *   anchor_rows host int32 [k_anchors], strictly ascending in [0, R); 1 <= k < R.
- *   lse_work    float [H][N], device, caller-owned workspace: overwritten (for
- *               the listed heads) with each query's base-2 log-sum-exp of
- *               scale * q . k over all keys.
  *   row_sim     float [H][F][R], device, written for the listed heads.
  *   heads       host int32 [n_heads] or NULL for all heads.
- * Asynchronous. calibatt_set_kernel_events times the similarity kernel.
+ * Asynchronous. calibatt_set_kernel_events times the similarity launch.
  */
 calibatt_status_t calibatt_spatial_similarity(const void* q, const void* k, int32_t H, int32_t N, int32_t d,
                                               calibatt_dtype_t dtype, float scale, int32_t F, int32_t R,
                                               int32_t C, const int32_t* anchor_rows, int32_t k_anchors,
-                                              float* lse_work, float* row_sim, const int32_t* heads,
-                                              int32_t n_heads, void* stream);
+                                              float* row_sim, const int32_t* heads, int32_t n_heads,
+                                              void* stream);
 
 /*
  * Repetition flags ([Notes] Key Design 3: the similarities are averaged over

@@ -199,12 +199,14 @@ def test_spatial_similarity_rejects():
     f = lib.calibatt_spatial_similarity
     def call(**kw):
         a = dict(q=P, k=P, H=1, N=600, d=64, dtype=cal.BF16, scale=0.125, F=3, R=10, C=20,
-                 anchors=anchors.ctypes.data, ka=2, lse=P, sim=P)
+                 anchors=anchors.ctypes.data, ka=2, sim=P)
         a.update(kw)
         return f(a["q"], a["k"], a["H"], a["N"], a["d"], a["dtype"], a["scale"], a["F"], a["R"], a["C"],
-                 a["anchors"], a["ka"], a["lse"], a["sim"], None, 0, None)
-    assert call(lse=None) == INVALID and "lse_work" in cal.last_error()
+                 a["anchors"], a["ka"], a["sim"], None, 0, None)
     assert call(sim=None) == INVALID
+    assert call(q=None) == INVALID
+    unsorted = np.array([7, 2], dtype=np.int32)
+    assert call(anchors=unsorted.ctypes.data) == INVALID and "ascending" in cal.last_error()
     assert call(N=601) == INVALID and "F*R*C" in cal.last_error()
     assert call(d=32) == INVALID
     every = np.arange(10, dtype=np.int32)

@@ -22,10 +22,8 @@ TOL_SIM = 1e-5
 
 def _sims(q, k, F, R, C, anchors, dtype, scale=None):
     H, N, d = q.shape
-    lse = torch.full((H, N), float("nan"), dtype=torch.float32, device="cuda")
     sim = torch.full((H, F, R), float("nan"), dtype=torch.float32, device="cuda")
-    cal.calibatt_spatial_similarity(to_device(q, dtype), to_device(k, dtype), F, R, C, anchors, lse, sim,
-                                    scale=scale)
+    cal.calibatt_spatial_similarity(to_device(q, dtype), to_device(k, dtype), F, R, C, anchors, sim, scale=scale)
     torch.cuda.synchronize()
     return sim.cpu().numpy().astype(np.float64)
 
@@ -59,9 +57,8 @@ def test_head_subset_leaves_other_heads():
     q, k = workloads.make_calibration_prompts(N, d, F, R, C, H, 1, seed=9300)
     q, k = q[0], k[0]
     scale = float(np.float32(1.0 / np.sqrt(d)))
-    lse = torch.full((H, N), float("nan"), dtype=torch.float32, device="cuda")
     sim = torch.full((H, F, R), float("nan"), dtype=torch.float32, device="cuda")
-    cal.calibatt_spatial_similarity(to_device(q, "bf16"), to_device(k, "bf16"), F, R, C, anchors, lse, sim,
+    cal.calibatt_spatial_similarity(to_device(q, "bf16"), to_device(k, "bf16"), F, R, C, anchors, sim,
                                     heads=[2, 0], scale=scale)
     torch.cuda.synchronize()
     got = sim.cpu().numpy().astype(np.float64)
@@ -130,11 +127,10 @@ def test_repetition_chain_agrees_with_oracle():
     anchors = [2, 7]
     q, k = workloads.make_calibration_prompts(N, d, F, R, C, H, P, seed=9900)
     scale = float(np.float32(1.0 / np.sqrt(d)))
-    lse = torch.empty((H, N), dtype=torch.float32, device="cuda")
     sims = torch.empty((P, H, F, R), dtype=torch.float32, device="cuda")
     want = np.empty((P, H, F, R))
     for p in range(P):
-        cal.calibatt_spatial_similarity(to_device(q[p], "bf16"), to_device(k[p], "bf16"), F, R, C, anchors, lse,
+        cal.calibatt_spatial_similarity(to_device(q[p], "bf16"), to_device(k[p], "bf16"), F, R, C, anchors,
                                         sims[p], scale=scale)
         for h in range(H):
             want[p, h] = oracle.row_similarity(exact_values(q[p, h], "bf16"), exact_values(k[p, h], "bf16"), F, R, C,
