@@ -21,7 +21,7 @@ from ._lib import (BF16, F32, CalibattError, IntervalList, IntervalListView, Ski
                    calibatt_compile_intervals, calibatt_compile_skiplist, calibatt_layer_dispatch,
                    calibatt_layer_dispatch_iv, calibatt_repetition_flags, calibatt_set_kernel_events,
                    calibatt_spatial_similarity, calibatt_version,
-                   compile_intervals, compile_skiplist, last_error)
+                   compile_intervals, compile_skiplist, energy_work_bytes, last_error)
 
 __all__ = ["BF16", "F32", "CalibattError", "IntervalList", "IntervalListView", "SkipList", "SkipListView",
            "calibatt_anchor_attn", "calibatt_block_energy", "calibatt_block_sparse_attn",
@@ -29,4 +29,4 @@ __all__ = ["BF16", "F32", "CalibattError", "IntervalList", "IntervalListView", "
            "calibatt_compile_intervals", "calibatt_compile_skiplist", "calibatt_layer_dispatch",
            "calibatt_layer_dispatch_iv", "calibatt_repetition_flags", "calibatt_set_kernel_events",
            "calibatt_spatial_similarity", "calibatt_version",
-           "compile_intervals", "compile_skiplist", "last_error"]
+           "compile_intervals", "compile_skiplist", "energy_work_bytes", "last_error"]

@@ -81,7 +81,7 @@ def _load():
                                                ctypes.POINTER(IntervalListView), i32, i32, vp,
                                                i32, i32, i32, vp, i32, vp]
     lib.calibatt_layer_dispatch_iv.restype = i32
-    lib.calibatt_block_energy.argtypes = [vp, vp, i32, i32, i32, i32, f32, i32, vp, vp, i32, vp]
+    lib.calibatt_block_energy.argtypes = [vp, vp, i32, i32, i32, i32, f32, i32, vp, vp, i32, vp, i64, vp]
     lib.calibatt_block_energy.restype = i32
     lib.calibatt_select_blocks.argtypes = [vp, i64, i32, f32, vp, vp, vp]
     lib.calibatt_select_blocks.restype = i32
@@ -305,13 +305,25 @@ def calibatt_layer_dispatch_iv(q, k, v, o, lse, il: IntervalList, t: int, l: int
                                           flags.ctypes.data, F, R, C, aarr.ctypes.data, ka, _stream(stream)))
 
 
-def calibatt_block_energy(q, k, energy, B: int, heads=None, scale: float | None = None, stream=None) -> None:
-    """Block energies [H, nb, nb] (float32 device tensor) of one prompt's q, k [H, N, d]."""
+def energy_work_bytes(N: int, B: int, heads: int = 1) -> int:
+    """Workspace bytes for a one-pass calibatt_block_energy launch of `heads` heads."""
+    nb = -(-N // B)
+    return nb * nb * B * 4 * heads
+
+
+def calibatt_block_energy(q, k, energy, B: int, heads=None, scale: float | None = None, work=None,
+                          stream=None) -> None:
+    """Block energies [H, nb, nb] (float32 device tensor) of one prompt's q, k [H, N, d].
+
+    work: optional device tensor used as the one-pass workspace (its whole storage).
+    """
     H, N, d = q.shape
     scale = float(np.float32(1.0 / np.sqrt(d))) if scale is None else scale
     harr, nh = _host_i32(heads)
+    wbytes = 0 if work is None else work.numel() * work.element_size()
     _check(lib.calibatt_block_energy(_ptr(q), _ptr(k), H, N, d, _dtype_code(q), scale, B, _ptr(energy),
-                                     harr.ctypes.data if harr is not None else None, nh, _stream(stream)))
+                                     harr.ctypes.data if harr is not None else None, nh, _ptr(work), wbytes,
+                                     _stream(stream)))
 
 
 def calibatt_select_blocks(energy, tau: float, mask=None, counts=None, stream=None) -> None:

@@ -4,6 +4,7 @@
 // assume what these checks establish (sizes, supported d and block sizes,
 // head and anchor ranges). The only synchronisation in the library is the
 // read-back of the entry count in the two compile calls.
+#include <algorithm>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -381,7 +382,8 @@ calibatt_status_t calibatt_layer_dispatch_iv(const void* q, const void* k, const
 
 calibatt_status_t calibatt_block_energy(const void* q, const void* k, int32_t H, int32_t N, int32_t d,
                                         calibatt_dtype_t dtype, float scale, int32_t B, float* energy,
-                                        const int32_t* heads, int32_t n_heads, void* stream) {
+                                        const int32_t* heads, int32_t n_heads, float* work, int64_t work_bytes,
+                                        void* stream) {
   // (v and o are not used: the placeholders pass the shared tensor checks)
   calibatt_status_t st = check_tensors(q, k, q, energy, H, N, d, dtype, scale);
   if (st != CALIBATT_OK) return st;
@@ -390,25 +392,38 @@ calibatt_status_t calibatt_block_energy(const void* q, const void* k, int32_t H,
   if (nb > CALIBATT_MAX_NB) return fail(CALIBATT_ERR_INVALID_ARG, "nb exceeds %d", CALIBATT_MAX_NB);
   std::vector<int32_t> hs;
   if ((st = check_heads(heads, n_heads, H, hs)) != CALIBATT_OK) return st;
+  // one-pass workspace: nb * nb * B floats per head of a launch (bf16 only)
+  const int64_t per_head = nb * nb * B * (int64_t)sizeof(float);
+  const bool one_pass = work != nullptr && dtype == CALIBATT_BF16;
+  if (work && work_bytes < per_head)
+    return fail(CALIBATT_ERR_INVALID_ARG, "work_bytes %lld < %lld (nb*nb*B floats, one head)", (long long)work_bytes,
+                (long long)per_head);
+  if (reinterpret_cast<uintptr_t>(work) % 16 != 0) return fail(CALIBATT_ERR_INVALID_ARG, "work is not 16-byte aligned");
+  const int64_t chunk = one_pass ? std::min<int64_t>((int64_t)hs.size(), work_bytes / per_head) : (int64_t)hs.size();
   calibatt::EnergyParams p;
   std::memset(&p, 0, sizeof(p));
   p.q = q;
   p.k = k;
   p.energy = energy;
+  p.work = one_pass ? work : nullptr;
   p.head_stride = (int64_t)N * d;
   p.N = N;
   p.nb = (int32_t)nb;
   p.scale = scale;
   p.scale_log2 = scale * 1.4426950408889634f;
   p.dtype_f32 = dtype == CALIBATT_F32 ? 1 : 0;
-  p.n_heads = (int32_t)hs.size();
-  for (size_t i = 0; i < hs.size(); ++i) p.heads[i] = hs[i];
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipEvent_t eb = g_ev_begin, ee = g_ev_end;
   g_ev_begin = g_ev_end = nullptr;
   hipError_t e;
   if (eb && (e = hipEventRecord(eb, s)) != hipSuccess) return hip_fail(e, "hipEventRecord");
-  if ((e = calibatt::launch_energy(p, d, B, s)) != hipSuccess) return hip_fail(e, "block energy kernel launch");
+  // heads in launches of at most `chunk` (the workspace holds one launch)
+  for (size_t h0 = 0; h0 < hs.size(); h0 += (size_t)std::max<int64_t>(chunk, 1)) {
+    const size_t h1 = std::min(hs.size(), h0 + (size_t)std::max<int64_t>(chunk, 1));
+    p.n_heads = (int32_t)(h1 - h0);
+    for (size_t i = h0; i < h1; ++i) p.heads[i - h0] = hs[i];
+    if ((e = calibatt::launch_energy(p, d, B, s)) != hipSuccess) return hip_fail(e, "block energy kernel launch");
+  }
   if (ee && (e = hipEventRecord(ee, s)) != hipSuccess) return hip_fail(e, "hipEventRecord");
   return ok();
 }

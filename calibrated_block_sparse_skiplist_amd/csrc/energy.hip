@@ -6,11 +6,16 @@
 // Block energy (Eq. 5): for query block r and key block c of one head,
 //   E[r][c] = (1 / |I_r|) * sum_{i in I_r} sum_{j in J_c} P[i][j],
 // P = softmax over all N keys of scale * q_i . k_j. The full P is never
-// stored: one workgroup owns one query block and streams every key block
-// twice. Pass 1 finds each query's log-sum-exp; pass 2 recomputes the scores,
-// turns them into probabilities with that log-sum-exp and adds them up per key
-// block. Rows of a partial last query block are averaged over their actual
-// count, so every row of E sums to one.
+// stored: one workgroup owns one query block. Without a workspace it streams
+// every key block twice: pass 1 finds each query's log-sum-exp, pass 2
+// recomputes the scores, turns them into probabilities with that log-sum-exp
+// and adds them up per key block. With a workspace it streams the keys once:
+// each query keeps its log-sum-exp running and leaves, per key block, the
+// base-2 log of its sum over that block (relative to its first reference
+// maximum) in the workspace; once the query's total is known, the block sums
+// are normalised and added up over the block's queries. Rows of a partial last
+// query block are averaged over their actual count, so every row of E sums to
+// one.
 //
 // Selection (Key Design 1): per row of E, sort energies descending (ties to
 // the lower key block), keep the shortest prefix whose cumulative mass reaches
@@ -31,6 +36,9 @@ namespace {
 using namespace dev;
 
 constexpr int kPrefetch = 4;            // K operand reads in flight ahead of their MFMA
+// One-pass kernel: a reference maximum moves only when a stage's scores pass
+// it by more than this (log2 units), so terms stay <= 2^8.
+constexpr float kRescaleThreshold = 8.0f;
 
 // ---------------------------------------------------------------------------
 // bf16 energies: S^T = K Q^T with v_mfma_f32_32x32x16_bf16 exactly as in the
@@ -224,6 +232,176 @@ __global__ __launch_bounds__(BLK * 2) void energy_bf16_kernel(const EnergyParams
   }
 }
 
+// One pass with a workspace p.work of [items][nb][BLK] floats (item = index
+// of the head in p.heads * nb + query block). The two key-half lanes of a
+// query share a lazily moved reference maximum m; at the end of key block c,
+// lane h = 0 stores log2(sum over the block of exp2(s - m)) + (m - m0), m0 the
+// reference after the first stage. With the query's total
+// lse' = (m_end - m0) + log2(l), its probability mass in block c is
+// exp2(stored - lse'); one wave per key block adds those up over the block's
+// queries in a fixed order.
+template <int D, int BLK>
+__global__ __launch_bounds__(BLK * 2) void energy_bf16_onepass_kernel(const EnergyParams p) {
+  constexpr int NW = BLK / 32;
+  constexpr int SUB = 64;
+  constexpr int SPB = BLK / SUB;
+  constexpr int CPR = D / 8;
+  constexpr int KT = SUB / 32;
+  constexpr int DS = D / 16;
+  constexpr int STAGE = SUB * CPR;
+  constexpr int LPW = STAGE / 64 / NW;   // copy instructions per wave and stage
+  constexpr int RPI = 64 / CPR;
+
+  __shared__ uint4 lds_k[2 * STAGE];
+  __shared__ float lds_lse[BLK];
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int h = lane >> 5;
+  const int l32 = lane & 31;
+  const int nb = p.nb;
+  int n_tok = p.N;
+  float scale_log2 = p.scale_log2;
+  asm volatile("" : "+s"(n_tok), "+s"(scale_log2));
+
+  const int64_t item = xcd_item(blockIdx.x, gridDim.x, 32);
+  const int head = p.heads[item / nb];
+  const int r = (int)(item % nb);
+  const u16* Q = static_cast<const u16*>(p.q) + (int64_t)head * p.head_stride;
+  const char* Kb = reinterpret_cast<const char*>(static_cast<const u16*>(p.k) + (int64_t)head * p.head_stride);
+  float* ws = p.work + item * (int64_t)nb * BLK;
+
+  const int qtok = r * BLK + wave * 32 + l32;
+  const bool q_ok = qtok < n_tok;
+  bf16x8 qf[DS];
+#pragma unroll
+  for (int s = 0; s < DS; ++s) {
+    uint4 raw = make_uint4(0, 0, 0, 0);
+    if (q_ok) raw = ld_global16(Q + (int64_t)qtok * D + 16 * s + 8 * h);
+    qf[s] = bitcast<bf16x8>(raw);
+  }
+
+  const int dq = lane / CPR;
+  const int dpos = lane % CPR;
+  const uint32_t dma_lane = (uint32_t)(dq * 2 * D + 16 * (dpos ^ (dq & (CPR - 1))));
+  const uint32_t k_lane = (uint32_t)(l32 * 2 * D + 16 * (h ^ (l32 & (CPR - 1))));
+  auto issue = [&](int stage, int i, uint4* dst) {
+    const int row0 = stage * SUB;
+    const int rr = (wave * LPW + i) * RPI;
+    const uint32_t off = dma_lane ^ (uint32_t)(16 * (rr & (CPR - 1)));
+    if (row0 + SUB <= n_tok) {
+      dma16(Kb + (int64_t)(row0 + rr) * (2 * D), off, dst + (wave * LPW + i) * 64);
+    } else {
+      asm volatile("");
+      const int b0 = min(row0, n_tok - 1);
+      const int grow = min(row0 + rr + dq, n_tok - 1);
+      dma16(Kb + (int64_t)b0 * (2 * D), (uint32_t)((grow - b0) * (2 * D)) + (off & (2 * D - 1)),
+            dst + (wave * LPW + i) * 64);
+    }
+  };
+
+  const int n_stages = nb * SPB;
+  float m_run = -INFINITY, m0 = 0.0f, l_run = 0.0f, b_run = 0.0f;
+#pragma unroll
+  for (int i = 0; i < LPW; ++i) issue(0, i, lds_k);
+  for (int j = 0; j < n_stages; ++j) {
+    const uint4* sk = lds_k + (j & 1) * STAGE;
+    uint4* nk = lds_k + ((j + 1) & 1) * STAGE;
+    wait_vmcnt<0>();
+    barrier_no_fence();
+    const bool has_next = j + 1 < n_stages;
+
+    f32x16 sacc[KT];
+    {
+      auto read_k = [&](int idx) -> bf16x8 {
+        const int t = idx / DS, s = idx % DS;
+        const char* ptr = reinterpret_cast<const char*>(sk) + 32 * t * (2 * D) + (k_lane ^ (uint32_t)(32 * s));
+        return bitcast<bf16x8>(*reinterpret_cast<const uint4*>(ptr));
+      };
+      constexpr int kEvery = (KT * DS) / LPW > 0 ? (KT * DS) / LPW : 1;
+      bf16x8 ring[kPrefetch];
+#pragma unroll
+      for (int i = 0; i < kPrefetch; ++i) ring[i] = read_k(i);
+#pragma unroll
+      for (int idx = 0; idx < KT * DS; ++idx) {
+        const int t = idx / DS, s = idx % DS;
+        const bf16x8 a = ring[idx % kPrefetch];
+        if (idx + kPrefetch < KT * DS) ring[idx % kPrefetch] = read_k(idx + kPrefetch);
+        sacc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[s], s == 0 ? f32x16{} : sacc[t], 0, 0, 0);
+        if (has_next && idx % kEvery == kEvery - 1 && idx / kEvery < LPW) issue(j + 1, idx / kEvery, nk);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      if (has_next) {
+#pragma unroll
+        for (int i = (KT * DS) / kEvery; i < LPW; ++i) issue(j + 1, i, nk);
+      }
+    }
+    const int valid = n_tok - j * SUB;
+    if (valid < SUB) {
+      int lv = valid - 4 * h;
+      asm volatile("" : "+v"(lv));
+#pragma unroll
+      for (int t = 0; t < KT; ++t)
+#pragma unroll
+        for (int a = 0; a < 16; ++a) {
+          const int key = 32 * t + 8 * (a >> 2) + (a & 3);
+          if (key >= lv) sacc[t][a] = -INFINITY;
+        }
+    }
+
+    float mx = -INFINITY;
+#pragma unroll
+    for (int t = 0; t < KT; ++t)
+#pragma unroll
+      for (int a = 0; a < 16; ++a) mx = fmaxf(mx, sacc[t][a]);
+    const float mb = mx * scale_log2;
+    // (key 0 is in every query's first stage, so m is finite from stage 0 on)
+    if (__ballot(mb > m_run + kRescaleThreshold) != 0) {
+      asm volatile("");   // rare: keep it a branch
+      const float m_new = fmaxf(m_run, fmaxf(mb, __shfl_xor(mb, 32)));
+      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);   // 0 while m_run is -inf
+      l_run *= alpha;
+      b_run *= alpha;
+      m_run = m_new;
+    }
+    if (j == 0) m0 = m_run;
+    const float neg_m = -m_run;
+    float s0 = 0.0f, s1 = 0.0f;
+#pragma unroll
+    for (int t = 0; t < KT; ++t)
+#pragma unroll
+      for (int a = 0; a < 16; a += 2) {
+        s0 += __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[t][a], scale_log2, neg_m));
+        s1 += __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[t][a + 1], scale_log2, neg_m));
+      }
+    b_run += s0 + s1;
+    if (j % SPB == SPB - 1) {
+      // key block c = j / SPB done: both key halves of the query, same reference
+      const float bsum = b_run + __shfl_xor(b_run, 32);
+      if (h == 0) ws[(int64_t)(j / SPB) * BLK + wave * 32 + l32] = __log2f(bsum) + (m_run - m0);
+      l_run += b_run;
+      b_run = 0.0f;
+    }
+  }
+  const float l_tot = l_run + __shfl_xor(l_run, 32);
+  // queries past N get +inf, so every probability of theirs is exactly 0
+  if (h == 0) lds_lse[wave * 32 + l32] = q_ok ? (m_run - m0) + __log2f(l_tot) : INFINITY;
+  __syncthreads();   // (also orders every wave's workspace stores before the reads below)
+
+  const int n_q = min(BLK, n_tok - r * BLK);
+  const float inv = 1.0f / (float)n_q;
+  float* out = p.energy + ((int64_t)head * nb + r) * nb;
+  for (int c = wave; c < nb; c += NW) {
+    float v = 0.0f;
+#pragma unroll
+    for (int q = lane; q < BLK; q += 64)
+      v += __builtin_amdgcn_exp2f(ws[(int64_t)c * BLK + q] - lds_lse[q]);
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off);
+    if (lane == 0) out[c] = v * inv;
+  }
+}
+
 // fp32 energies: one thread per query, K tiles in LDS read as broadcasts,
 // fp32 FMA and expf; the same two passes.
 template <int D, int BLK>
@@ -358,7 +536,10 @@ template <int D, int BLK>
 hipError_t launch_energy_typed(const EnergyParams& p, hipStream_t s) {
   const int64_t items = (int64_t)p.n_heads * p.nb;
   if (items == 0) return hipSuccess;
-  if (p.dtype_f32) {
+  if (p.work && !p.dtype_f32) {
+    auto kern = energy_bf16_onepass_kernel<D, BLK>;
+    hipLaunchKernelGGL(kern, dim3((unsigned)items), dim3(BLK * 2), 0, s, p);
+  } else if (p.dtype_f32) {
     const size_t smem = (size_t)(BLK * D + BLK) * sizeof(float);
     auto kern = energy_f32_kernel<D, BLK>;
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),

@@ -71,6 +71,7 @@ struct EnergyParams {
   const void* q;
   const void* k;
   float* energy;            // [H][nb][nb]
+  float* work;              // bf16 one-pass kernel: [n_heads][nb][nb][B] floats, or null (two passes)
   int64_t head_stride;      // N * d elements
   int32_t N;
   int32_t nb;

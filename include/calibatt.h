@@ -231,12 +231,20 @@ calibatt_status_t calibatt_layer_dispatch_iv(const void* q, const void* k, const
  *   B         64 or 128 (query and key block size); nb = ceil(N/B) <= CALIBATT_MAX_NB.
  *   energy    float [H][nb][nb], device; rows of the listed heads are written.
  *   heads     host int32 [n_heads] or NULL for all heads.
- * Asynchronous; the kernel reads K twice (one pass for each query's
- * log-sum-exp, one for the sums). calibatt_set_kernel_events applies to it.
+ *   work      optional device workspace (16-byte aligned, caller-owned,
+ *             overwritten), work_bytes its size. NULL: every score is computed
+ *             twice (a pass for each query's log-sum-exp, then the sums).
+ *             Given (bf16 inputs): one pass; each query leaves one float per
+ *             key block in the workspace (nb*nb*B floats per head, 179 MB for
+ *             a head of N = 75,600 at B = 128), and the listed heads run in
+ *             launches of as many heads as it holds. work_bytes below one
+ *             head's share is an error. fp32 inputs ignore it.
+ * Asynchronous. calibatt_set_kernel_events times all of its launches.
  */
 calibatt_status_t calibatt_block_energy(const void* q, const void* k, int32_t H, int32_t N, int32_t d,
                                         calibatt_dtype_t dtype, float scale, int32_t B, float* energy,
-                                        const int32_t* heads, int32_t n_heads, void* stream);
+                                        const int32_t* heads, int32_t n_heads, float* work, int64_t work_bytes,
+                                        void* stream);
 
 /*
  * Per-prompt selection ([Notes] Key Design 1): for every row of `energy`

@@ -171,10 +171,21 @@ def test_block_energy_rejects(kw, msg):
     a = dict(q=P, k=P, H=2, N=1000, d=128, dtype=cal.BF16, scale=0.088, B=128, energy=P)
     a.update(kw)
     st = lib.calibatt_block_energy(a["q"], a["k"], a["H"], a["N"], a["d"], a["dtype"], a["scale"], a["B"],
-                                   a["energy"], None, 0, None)
+                                   a["energy"], None, 0, None, 0, None)
     assert st == INVALID and msg in cal.last_error()
     bad = np.array([2], dtype=np.int32)
-    assert lib.calibatt_block_energy(P, P, 2, 1000, 128, cal.BF16, 0.088, 128, P, bad.ctypes.data, 1, None) == INVALID
+    assert lib.calibatt_block_energy(P, P, 2, 1000, 128, cal.BF16, 0.088, 128, P, bad.ctypes.data, 1, None, 0,
+                                     None) == INVALID
+
+
+def test_block_energy_workspace_rejects():
+    need = cal.energy_work_bytes(1000, 128)                # 8 * 8 * 128 floats for one head
+    assert need == 8 * 8 * 128 * 4
+    f = lib.calibatt_block_energy
+    assert f(P, P, 2, 1000, 128, cal.BF16, 0.088, 128, P, None, 0, P, need - 4, None) == INVALID
+    assert "work_bytes" in cal.last_error()
+    assert f(P, P, 2, 1000, 128, cal.BF16, 0.088, 128, P, None, 0, P + 4, need, None) == INVALID
+    assert "aligned" in cal.last_error()
 
 
 @pytest.mark.parametrize("args,msg", [

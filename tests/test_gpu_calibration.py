@@ -7,7 +7,8 @@ threshold.
 Energy tolerance: the kernel multiplies exact bf16 (or fp32) inputs with fp32
 accumulation, evaluates exp2 in fp32 and sums up to N*B probabilities per entry
 in fp32; the error of an entry stays a few 1e-6 for E <= 1, so 2e-5 absolute
-is used (entries and row sums).
+is used (entries and row sums). The one-pass form (with a workspace) adds one
+fp32 log2/exp2 round trip per (query, key block), ~1e-7 relative.
 """
 import numpy as np
 import pytest
@@ -29,19 +30,21 @@ def _energy_case(N, d, B, dtype, H=2, seed=0, geom=None):
     return q[0], k[0]
 
 
+@pytest.mark.parametrize("one_pass", [False, True])
 @pytest.mark.parametrize("N,d,B,dtype,geom", [
     (1000, 128, 128, "bf16", (4, 10, 25)), (1000, 64, 128, "bf16", (4, 10, 25)), (700, 128, 64, "bf16", (7, 10, 10)),
     (700, 64, 64, "bf16", (7, 10, 10)), (77, 128, 128, "bf16", None), (5, 64, 64, "bf16", None),
     (3000, 128, 128, "bf16", (5, 20, 30)), (1000, 64, 64, "f32", (4, 10, 25)), (300, 128, 128, "f32", None),
 ])
-def test_block_energy_small(N, d, B, dtype, geom):
-    say(f"[energy] N={N} d={d} B={B} {dtype}")
+def test_block_energy_small(N, d, B, dtype, geom, one_pass):
+    say(f"[energy] N={N} d={d} B={B} {dtype} one_pass={one_pass}")
     H = 2
     q, k = _energy_case(N, d, B, dtype, H=H, seed=N + d, geom=geom)
     nb = -(-N // B)
     e = torch.full((H, nb, nb), float("nan"), dtype=torch.float32, device="cuda")
     scale = float(np.float32(1.0 / np.sqrt(d)))
-    cal.calibatt_block_energy(to_device(q, dtype), to_device(k, dtype), e, B, scale=scale)
+    work = _work(N, B, H) if one_pass else None
+    cal.calibatt_block_energy(to_device(q, dtype), to_device(k, dtype), e, B, scale=scale, work=work)
     torch.cuda.synchronize()
     eg = e.cpu().numpy().astype(np.float64)
     for h in range(H):
@@ -50,6 +53,57 @@ def test_block_energy_small(N, d, B, dtype, geom):
         say(f"  head {h}: max|dE| = {err:.2e}")
         assert err <= TOL_E, (h, err)
         np.testing.assert_allclose(eg[h].sum(axis=1), 1.0, atol=TOL_E)
+
+
+def _work(N, B, heads):
+    """A workspace for `heads` heads, filled with NaN so that an unwritten entry shows."""
+    return torch.full((cal.energy_work_bytes(N, B, heads) // 4,), float("nan"), dtype=torch.float32, device="cuda")
+
+
+def test_block_energy_one_pass_in_chunks():
+    N, d, B, H = 1000, 128, 128, 3
+    q, k = _energy_case(N, d, B, "bf16", H=H, seed=11, geom=(4, 10, 25))
+    nb = -(-N // B)
+    dq, dk = to_device(q, "bf16"), to_device(k, "bf16")
+    scale = float(np.float32(1.0 / np.sqrt(d)))
+    e1 = torch.full((H, nb, nb), -7.0, dtype=torch.float32, device="cuda")
+    e2 = torch.full((H, nb, nb), -7.0, dtype=torch.float32, device="cuda")
+    cal.calibatt_block_energy(dq, dk, e1, B, heads=[2, 0, 1], scale=scale, work=_work(N, B, 1))   # three launches
+    cal.calibatt_block_energy(dq, dk, e2, B, heads=[2, 0, 1], scale=scale, work=_work(N, B, 1))
+    torch.cuda.synchronize()
+    assert torch.equal(e1.view(torch.int32), e2.view(torch.int32))    # run-to-run identical
+    eg = e1.cpu().numpy().astype(np.float64)
+    for h in range(H):
+        want = oracle.block_energy(exact_values(q[h], "bf16"), exact_values(k[h], "bf16"), B, scale)
+        assert float(np.max(np.abs(eg[h] - want))) <= TOL_E, h
+
+
+@pytest.mark.parametrize("kind", ["rising", "large"])
+def test_block_energy_one_pass_moving_maximum(kind):
+    """Scores that rise along the keys (by ~35 in log2 units) move each query's reference maximum
+    several times; large logits (reference maxima ~40 in log2 units) test the stored per-block logs."""
+    N, d, B, H = 1500, 64, 64, 2
+    rng = np.random.default_rng(77 if kind == "rising" else 78)
+    q = rng.standard_normal((H, N, d)).astype(np.float32)
+    k = rng.standard_normal((H, N, d)).astype(np.float32)
+    if kind == "rising":
+        q = np.abs(q) * 0.6
+        k = np.abs(k) * np.linspace(0.05, 8.0, N, dtype=np.float32)[None, :, None]
+    else:
+        q *= 3.0
+        k *= 3.0
+    qb, kb = workloads.bf16_bits(q), workloads.bf16_bits(k)
+    nb = -(-N // B)
+    scale = float(np.float32(1.0 / np.sqrt(d)))
+    e = torch.full((H, nb, nb), float("nan"), dtype=torch.float32, device="cuda")
+    cal.calibatt_block_energy(to_device(qb, "bf16"), to_device(kb, "bf16"), e, B, scale=scale, work=_work(N, B, H))
+    torch.cuda.synchronize()
+    eg = e.cpu().numpy().astype(np.float64)
+    for h in range(H):
+        want = oracle.block_energy(exact_values(qb[h], "bf16"), exact_values(kb[h], "bf16"), B, scale)
+        err = float(np.max(np.abs(eg[h] - want)))
+        say(f"  {kind} head {h}: max|dE| = {err:.2e}")
+        assert err <= TOL_E, (h, err)
 
 
 def test_block_energy_head_subset_and_determinism():
@@ -66,12 +120,14 @@ def test_block_energy_head_subset_and_determinism():
     assert torch.equal(e1.view(torch.int32), e2.view(torch.int32))    # run-to-run identical
 
 
-def test_block_energy_full_720p_head():
+@pytest.mark.parametrize("one_pass", [False, True])
+def test_block_energy_full_720p_head(one_pass):
     cfg = workloads.get_config("wan720")
-    say(f"[energy] 720p head: N={cfg.N}")
+    say(f"[energy] 720p head: N={cfg.N} one_pass={one_pass}")
     q, k = workloads.make_calibration_prompts(cfg.N, cfg.d, cfg.F, cfg.R, cfg.C, 1, 1, seed=6000)
     e = torch.empty((1, cfg.nb, cfg.nb), dtype=torch.float32, device="cuda")
-    cal.calibatt_block_energy(to_device(q[0], "bf16"), to_device(k[0], "bf16"), e, cfg.B)
+    work = _work(cfg.N, cfg.B, 1) if one_pass else None
+    cal.calibatt_block_energy(to_device(q[0], "bf16"), to_device(k[0], "bf16"), e, cfg.B, work=work)
     torch.cuda.synchronize()
     eg = e[0].cpu().numpy().astype(np.float64)
     assert np.all(eg >= 0)
