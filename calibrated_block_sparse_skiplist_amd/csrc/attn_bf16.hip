@@ -328,10 +328,26 @@ void attn_bf16_kernel(const AttnParams p) {
       }
     };
 
+    // Nearly every stage has a next stage and no clamped rows in either copy:
+    // then the copies run straight, without the per-copy tests of issue_dma
+    // (their branches cost more than the copies themselves). One uniform test
+    // per stage picks the form.
+    const bool plain = has_next && !ksrc.clamp && !vsrc.clamp;
+    auto issue_plain = [&](int d) {
+      if (d < LPW) {
+        const int r = (wave * LPW + d) * RPI;
+        dma16(ksrc.base + (int64_t)r * (2 * D), dma_k_lane ^ (uint32_t)(16 * (r & (CPR - 1))),
+              nk + (wave * LPW + d) * 64);
+      } else {
+        const int r = (wave * LPW + d - LPW) * RPI;
+        dma16(vsrc.base + (int64_t)r * (2 * D), dma_v_lane, nv + (wave * LPW + d - LPW) * 64);
+      }
+    };
+
     // ---- S^T = K Q^T: operand reads run kPrefetchK MFMAs ahead; the copy of
     // the next stage is issued in small steps between the MFMAs ----
     f32x16 sacc[KT];
-    {
+    auto qk_product = [&](auto issue) {
       // K operand of step (t, s): key 32*t + l32, chunk 2*s + h, swizzled
       // by l32 & (CPR-1); the chunk bits of s enter as an XOR with 32*s.
       auto read_k = [&](int idx) -> bf16x8 {
@@ -349,13 +365,15 @@ void attn_bf16_kernel(const AttnParams p) {
         const bf16x8 a = ring[idx % kPrefetchK];
         if (idx + kPrefetchK < KT * DS) ring[idx % kPrefetchK] = read_k(idx + kPrefetchK);
         sacc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[s], s == 0 ? f32x16{} : sacc[t], 0, 0, 0);
-        if (idx % kDmaEvery == kDmaEvery - 1 && idx / kDmaEvery < 2 * LPW) issue_dma(idx / kDmaEvery);
+        if (idx % kDmaEvery == kDmaEvery - 1 && idx / kDmaEvery < 2 * LPW) issue(idx / kDmaEvery);
         __builtin_amdgcn_sched_barrier(0);   // keep the read-ahead order as written
       }
       // (copies that did not fit between the MFMAs, if any)
 #pragma unroll
-      for (int d = (KT * DS) / kDmaEvery; d < 2 * LPW; ++d) issue_dma(d);
-    }
+      for (int d = (KT * DS) / kDmaEvery; d < 2 * LPW; ++d) issue(d);
+    };
+    if (plain) qk_product(issue_plain);
+    else qk_product(issue_dma);
 
     // ---- mask keys past N (last block only; a stage wholly past N, the
     // second half of a short last block, is masked entirely) ----

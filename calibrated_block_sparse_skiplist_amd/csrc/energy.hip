@@ -130,7 +130,9 @@ __global__ __launch_bounds__(BLK * 2) void energy_bf16_kernel(const EnergyParams
       const bool has_next = j + 1 < n_stages;
 
       f32x16 sacc[KT];
-      {
+      // copy i of the next stage: straight when that stage is full (nearly
+      // always), else with the clamp of issue(); none after the last stage
+      auto qk_product = [&](auto copy) {
         auto read_k = [&](int idx) -> bf16x8 {
           const int t = idx / DS, s = idx % DS;
           const char* ptr = reinterpret_cast<const char*>(sk) + 32 * t * (2 * D) + (k_lane ^ (uint32_t)(32 * s));
@@ -146,13 +148,22 @@ __global__ __launch_bounds__(BLK * 2) void energy_bf16_kernel(const EnergyParams
           const bf16x8 a = ring[idx % kPrefetch];
           if (idx + kPrefetch < KT * DS) ring[idx % kPrefetch] = read_k(idx + kPrefetch);
           sacc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[s], s == 0 ? f32x16{} : sacc[t], 0, 0, 0);
-          if (has_next && idx % kEvery == kEvery - 1 && idx / kEvery < LPW) issue(j + 1, idx / kEvery, nk);
+          if (idx % kEvery == kEvery - 1 && idx / kEvery < LPW) copy(idx / kEvery);
           __builtin_amdgcn_sched_barrier(0);
         }
-        if (has_next) {
 #pragma unroll
-          for (int i = (KT * DS) / kEvery; i < LPW; ++i) issue(j + 1, i, nk);
-        }
+        for (int i = (KT * DS) / kEvery; i < LPW; ++i) copy(i);
+      };
+      if (has_next && (j + 2) * SUB <= n_tok) {
+        const char* base = Kb + (int64_t)(j + 1) * SUB * (2 * D);
+        qk_product([&](int i) {
+          const int rr = (wave * LPW + i) * RPI;
+          dma16(base + (int64_t)rr * (2 * D), dma_lane ^ (uint32_t)(16 * (rr & (CPR - 1))), nk + (wave * LPW + i) * 64);
+        });
+      } else {
+        qk_product([&](int i) {
+          if (has_next) issue(j + 1, i, nk);
+        });
       }
       const int valid = n_tok - j * SUB;
       if (valid < SUB) {
@@ -312,7 +323,9 @@ __global__ __launch_bounds__(BLK * 2) void energy_bf16_onepass_kernel(const Ener
     const bool has_next = j + 1 < n_stages;
 
     f32x16 sacc[KT];
-    {
+    // copy i of the next stage: straight when that stage is full (nearly
+    // always), else with the clamp of issue(); none after the last stage
+    auto qk_product = [&](auto copy) {
       auto read_k = [&](int idx) -> bf16x8 {
         const int t = idx / DS, s = idx % DS;
         const char* ptr = reinterpret_cast<const char*>(sk) + 32 * t * (2 * D) + (k_lane ^ (uint32_t)(32 * s));
@@ -328,13 +341,22 @@ __global__ __launch_bounds__(BLK * 2) void energy_bf16_onepass_kernel(const Ener
         const bf16x8 a = ring[idx % kPrefetch];
         if (idx + kPrefetch < KT * DS) ring[idx % kPrefetch] = read_k(idx + kPrefetch);
         sacc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[s], s == 0 ? f32x16{} : sacc[t], 0, 0, 0);
-        if (has_next && idx % kEvery == kEvery - 1 && idx / kEvery < LPW) issue(j + 1, idx / kEvery, nk);
+        if (idx % kEvery == kEvery - 1 && idx / kEvery < LPW) copy(idx / kEvery);
         __builtin_amdgcn_sched_barrier(0);
       }
-      if (has_next) {
 #pragma unroll
-        for (int i = (KT * DS) / kEvery; i < LPW; ++i) issue(j + 1, i, nk);
-      }
+      for (int i = (KT * DS) / kEvery; i < LPW; ++i) copy(i);
+    };
+    if (has_next && (j + 2) * SUB <= n_tok) {
+      const char* base = Kb + (int64_t)(j + 1) * SUB * (2 * D);
+      qk_product([&](int i) {
+        const int rr = (wave * LPW + i) * RPI;
+        dma16(base + (int64_t)rr * (2 * D), dma_lane ^ (uint32_t)(16 * (rr & (CPR - 1))), nk + (wave * LPW + i) * 64);
+      });
+    } else {
+      qk_product([&](int i) {
+        if (has_next) issue(j + 1, i, nk);
+      });
     }
     const int valid = n_tok - j * SUB;
     if (valid < SUB) {
