@@ -43,6 +43,8 @@ def parse_args():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--protocol-reps", type=int, default=30,
+                    help="layer calls timed one by one, warm and cache-flushed (0: skip)")
     ap.add_argument("--config", default="wan720",
                     choices=["tiny", "wan480_sparse", "wan480_dual", "wan720"])
     ap.add_argument("--dense-reps", type=int, default=3, help="launches of the dense comparator")
@@ -522,6 +524,37 @@ def main():
     e1.record(stream)
     torch.cuda.synchronize()
     layer_ms = e0.elapsed_time(e1) / reps
+
+    # layer-call timing protocol: 5 warm-ups, then R calls timed one by one with HIP events, back to
+    # back (warm) and with 1 GiB written before each call (cold: more than the 256 MB MALL); the
+    # median and the minimum of each
+    protocol = None
+    if args.protocol_reps > 0:
+        flush = torch.empty(1 << 28, dtype=torch.float32, device=dev)
+
+        def dispatch():
+            cal.calibatt_layer_dispatch(q, k, v, o, lse, sl, 0, 0, wl.rep_flags, cfg.F, cfg.R, cfg.C, wl.anchors,
+                                        scale=wl.scale, stream=stream)
+
+        def timed(cold):
+            pairs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                     for _ in range(args.protocol_reps)]
+            for _ in range(5):
+                dispatch()
+            for a, b in pairs:
+                if cold:
+                    flush.fill_(1.0)
+                a.record(stream)
+                dispatch()
+                b.record(stream)
+            torch.cuda.synchronize()
+            return [a.elapsed_time(b) for a, b in pairs]
+
+        warm, cold = timed(False), timed(True)
+        protocol = {"reps": args.protocol_reps, "warmups": 5, "flush_bytes": flush.numel() * 4,
+                    "warm_median_ms": round(float(np.median(warm)), 3), "warm_min_ms": round(float(np.min(warm)), 3),
+                    "cold_median_ms": round(float(np.median(cold)), 3), "cold_min_ms": round(float(np.min(cold)), 3)}
+        del flush
     # compile alone
     t_c = time.perf_counter()
     for _ in range(5):
@@ -609,6 +642,7 @@ def main():
         "dense_same_kernel_ms": round(dense_ms, 3) if dense_ms else None,
         "dense_tflops": round(work["flops_dense"] / (dense_ms * 1e-3) / 1e12, 1) if dense_ms else None,
         "speedup_vs_dense": round(dense_ms / layer_ms, 3) if dense_ms else None,
+        "layer_call_protocol": protocol,
         "intervals": intervals,
         "sparsity": {"token_sparse_heads": work["token_sparsity_sparse_heads"],
                      "block_sparse_heads": work["block_sparsity_sparse_heads"],
