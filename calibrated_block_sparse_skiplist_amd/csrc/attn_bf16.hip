@@ -8,8 +8,9 @@
 //
 // Work decomposition. One workgroup owns one work item: a tile of BLK queries
 // of one head; its BLK/32 waves own 32 queries each. Two workgroups share a
-// CU (register budget capped at 256 per lane, 64 KB of LDS each), so each
-// SIMD runs two waves that cover each other's waits. Keys are visited in
+// CU (register budget capped at 256 per lane; 72 KB of LDS each: K and V
+// double buffers plus the item's staged key-block list), so each SIMD runs
+// two waves that cover each other's waits. Keys are visited in
 // stages of 64 (two per 128-key block). In stage j each wave
 //   1. computes S^T_j = K_j Q^T with v_mfma_f32_32x32x16_bf16 (A = K from LDS,
 //      B = Q^T held in registers): every lane owns one query column and half
@@ -28,7 +29,9 @@
 //      pipe keeps running while the wave computes probabilities.
 // K and V tiles move HBM -> LDS with global_load_lds_dwordx4 (no register
 // staging), issued between the S^T MFMAs of the stage before they are used;
-// s_waitcnt vmcnt plus a workgroup barrier publish each tile.
+// s_waitcnt vmcnt plus a workgroup barrier publish each tile. A stage whose
+// copies stay inside the sequence (nearly all) issues them straight; only a
+// stage reaching past N takes the form with per-copy clamps.
 //
 // LDS rows are XOR-swizzled in 16-byte chunks: K by (row & 15), so the 16
 // rows of an MFMA operand read hit distinct banks; V by 4*(row & 3), so the

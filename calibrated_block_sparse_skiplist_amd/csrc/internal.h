@@ -15,8 +15,9 @@ namespace calibatt {
 //     i % anchor_tiles of the gathered anchor queries (F*k*C of them, in
 //     (frame, anchor, column) order), visiting every key block;
 //   * block-sparse items follow: head sparse_heads[j / nb] visits the list of
-//     query block order[rec*nb + j % nb] (or j % nb when order is NULL).
-// Anchor tiles (every key block) come first. Grid blocks map to items
+//     query block j % nb (or order[rec*nb + j % nb] when use_order is set and
+//     order is given; the entry points leave use_order at 0).
+// Grid blocks map to items
 // XCD-aware: workgroups are dispatched round-robin over the 8 XCDs, so within
 // each run of 8 * xcd_group grid blocks XCD x receives xcd_group consecutive
 // items; neighbouring query blocks share most of their key blocks, which then

@@ -19,7 +19,9 @@
  * Conventions shared by every entry point
  *  - All array pointers are device pointers (hipMalloc / torch CUDA tensors)
  *    unless marked "host". The caller owns every buffer; the library never
- *    frees caller memory and keeps no state between calls.
+ *    frees caller memory and keeps no state between calls beyond two
+ *    thread-local items: the last error message and a pending
+ *    calibatt_set_kernel_events pair.
  *  - Tensors Q, K, V, O are [H][N][d], contiguous, row-major. Token order is
  *    n = (f*R + r)*C + c: frame f, spatial row r, column c.
  *  - Blocks: query/key block b covers tokens [b*B, min((b+1)*B, N));
@@ -71,7 +73,10 @@ typedef enum { CALIBATT_BF16 = 0, CALIBATT_F32 = 1 } calibatt_dtype_t;
  *             and its query block r is row id*nb + r.
  *   col_idx : int32 [row_ptr[T*L*H*nb]], each row's key blocks, ascending.
  *   order   : int32 [T*L*H*nb] or NULL; per record, query blocks by
- *             descending kept count (ties by index). Used only to order work.
+ *             descending kept count (ties by index), for callers that
+ *             schedule work by cost. The attention calls do not read it: they
+ *             visit query blocks in block order, where neighbours share key
+ *             blocks in cache (heaviest-first measured no faster).
  */
 typedef struct {
   int32_t T, L, H, N, B, nb;
@@ -171,7 +176,8 @@ calibatt_status_t calibatt_layer_dispatch(const void* q, const void* k, const vo
  *   iv_ptr : int64 [T*L*H*nb + 1]; row id*nb + r owns runs iv_ptr[row] .. iv_ptr[row+1]-1.
  *   iv     : uint32 [iv_ptr[T*L*H*nb]] packed runs.
  *   order  : int32 [T*L*H*nb] or NULL; the same heaviest-first order as the
- *            index-list form (by kept-block count).
+ *            index-list form (by kept-block count), likewise not read by the
+ *            attention calls.
  */
 typedef struct {
   int32_t T, L, H, N, B, nb;
