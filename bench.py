@@ -221,6 +221,14 @@ def dictionary_sweep(args):
             rows = masks.shape[1] * masks.shape[2] * cfg.nb
             n_iv = il.n_iv
             del il
+            # the compile oracle (plain numpy scan, one host core) on the same whole dictionary, once
+            # per sparsity point
+            oracle_compile_s = None
+            if rf == 0.0 and not args.no_cpu_baseline:
+                import oracle
+                t0 = time.perf_counter()
+                oracle.compile_skiplist(masks)
+                oracle_compile_s = round(time.perf_counter() - t0, 3)
             layer_ms, flops = [], 0.0
             for l in range(min(args.sweep_layers, cfg.L)):
                 a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -243,6 +251,7 @@ def dictionary_sweep(args):
                               "layers": cfg.L, "heads": cfg.H, "nnz": sl.nnz,
                               "block_sparsity": round(1.0 - float(masks.astype(np.float64).mean()), 4),
                               "compile_ms": round(compile_ms, 3),
+                              "compile_oracle_s_1core": oracle_compile_s,
                               "compile_GBps": round((2 * mask_bytes + out_bytes) / compile_ms / 1e6, 1),
                               "runs": n_iv, "compile_intervals_ms": round(compile_iv_ms, 3),
                               "list_MB_index_form": round((8 * (rows + 1) + 4 * sl.nnz) / 1e6, 2),

@@ -36,9 +36,9 @@ namespace {
 using namespace dev;
 
 constexpr int kPrefetch = 4;            // K operand reads in flight ahead of their MFMA
-// One-pass kernel: a reference maximum moves only when a stage's scores pass
-// it by more than this (log2 units), so terms stay <= 2^8.
-constexpr float kRescaleThreshold = 8.0f;
+// One-pass kernel: a lane's 32 terms of a stage may sum to at most this
+// against the reference maximum before the reference moves.
+constexpr float kStageSumCap = 8192.0f;
 
 // ---------------------------------------------------------------------------
 // bf16 energies: S^T = K Q^T with v_mfma_f32_32x32x16_bf16 exactly as in the
@@ -371,32 +371,42 @@ __global__ __launch_bounds__(BLK * 2) void energy_bf16_onepass_kernel(const Ener
         }
     }
 
-    float mx = -INFINITY;
+    // The stage's terms exp2(s - m) against the current reference m. The
+    // reference moves only when some lane's 32 terms sum past 2^13 or are not
+    // finite (the first stage, while m is still -inf; masked keys then give
+    // NaN): then m becomes the maximum so far and the terms are redone. So
+    // the row maximum is only searched on those rare stages, and every term
+    // that is kept is at most 2^13.
+    auto stage_terms = [&](float neg_m) {
+      float s0 = 0.0f, s1 = 0.0f;
 #pragma unroll
-    for (int t = 0; t < KT; ++t)
+      for (int t = 0; t < KT; ++t)
 #pragma unroll
-      for (int a = 0; a < 16; ++a) mx = fmaxf(mx, sacc[t][a]);
-    const float mb = mx * scale_log2;
-    // (key 0 is in every query's first stage, so m is finite from stage 0 on)
-    if (__ballot(mb > m_run + kRescaleThreshold) != 0) {
+        for (int a = 0; a < 16; a += 2) {
+          s0 += __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[t][a], scale_log2, neg_m));
+          s1 += __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[t][a + 1], scale_log2, neg_m));
+        }
+      return s0 + s1;
+    };
+    float st = stage_terms(-m_run);
+    if (__ballot(!(st <= kStageSumCap)) != 0) {
       asm volatile("");   // rare: keep it a branch
+      float mx = -INFINITY;
+#pragma unroll
+      for (int t = 0; t < KT; ++t)
+#pragma unroll
+        for (int a = 0; a < 16; ++a) mx = fmaxf(mx, sacc[t][a]);
+      const float mb = mx * scale_log2;
+      // (key 0 is in every query's first stage, so m is finite from stage 0 on)
       const float m_new = fmaxf(m_run, fmaxf(mb, __shfl_xor(mb, 32)));
       const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);   // 0 while m_run is -inf
       l_run *= alpha;
       b_run *= alpha;
       m_run = m_new;
+      st = stage_terms(-m_run);
     }
     if (j == 0) m0 = m_run;
-    const float neg_m = -m_run;
-    float s0 = 0.0f, s1 = 0.0f;
-#pragma unroll
-    for (int t = 0; t < KT; ++t)
-#pragma unroll
-      for (int a = 0; a < 16; a += 2) {
-        s0 += __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[t][a], scale_log2, neg_m));
-        s1 += __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[t][a + 1], scale_log2, neg_m));
-      }
-    b_run += s0 + s1;
+    b_run += st;
     if (j % SPB == SPB - 1) {
       // key block c = j / SPB done: both key halves of the query, same reference
       const float bsum = b_run + __shfl_xor(b_run, 32);
