@@ -17,9 +17,10 @@
 //      of the stage's keys;
 //   2. runs the online softmax in fp32: exp2 with log2(e) folded into the
 //      scale, per-lane partial row sums of the bf16-rounded probabilities that
-//      also feed the PV product, and a rescale of O only when some row maximum
-//      grows by more than 2^8 (the stale maximum is exact algebra: numerator
-//      and denominator share it);
+//      also feed the PV product, against a reference maximum that moves (and
+//      rescales O) only when a stage's probabilities sum past 2^13 in some
+//      lane (a stale reference is exact algebra: numerator and denominator
+//      share it);
 //   3. accumulates O^T += V_{j-1}^T P_{j-1}^T with the same MFMA, one stage
 //      behind: A = V^T read from row-major LDS by ds_read_b64_tr_b16 (16-bit
 //      transpose across 16-lane groups), B = P^T packed to bf16 straight from
@@ -44,7 +45,7 @@ namespace {
 using namespace dev;
 
 constexpr float kLn2 = 0.6931471805599453f;
-constexpr float kRescaleThreshold = 8.0f;   // log2 units: stale maxima are allowed 2^8 headroom
+constexpr float kStageSumCap = 8192.0f;     // a lane's 32 probabilities of a stage may sum to this
 constexpr int kPrefetchK = 4;               // K operand reads in flight ahead of their MFMA
 constexpr int kPrefetchV = 3;               // V operand reads (2 instructions each) in flight
 constexpr int kListCap = CALIBATT_MAX_NB;   // key-block indices staged in LDS per item (all of them)
@@ -394,60 +395,70 @@ void attn_bf16_kernel(const AttnParams p) {
         }
     }
 
-    // ---- online softmax (fp32, log2 domain, lazy rescale) ----
-    // Each lane holds half of a query's keys. The reference maximum m_run is
-    // shared by both halves and only moves when some lane's own maximum
-    // exceeds it by more than the threshold; only then are the two halves
-    // combined (the common case needs no exchange between lanes). A moved
-    // reference scales O and l by alpha after the pending PV product, whose
-    // terms, like O, are relative to the old reference.
-    float mx = -INFINITY;
-#pragma unroll
-    for (int t = 0; t < KT; ++t)
-#pragma unroll
-      for (int a = 0; a < 16; ++a) mx = fmaxf(mx, sacc[t][a]);
-    const float mb = mx * scale_log2;
-    const bool moved = __ballot(mb > m_run + kRescaleThreshold) != 0;
-    float alpha = 1.0f;
-    if (moved) {
-      const float m_new = fmaxf(m_run, fmaxf(mb, __shfl_xor(mb, 32)));
-      alpha = __builtin_amdgcn_exp2f(m_run - m_new);   // 0 while m_run is -inf
-      m_run = m_new;
-    }
+    // ---- online softmax (fp32, log2 domain, lazy reference maximum) ----
+    // Probabilities of stage j are formed against the reference m_run shared
+    // by both key halves of a query, between the PV MFMAs of stage j-1. The
+    // reference moves only when some lane's 32 probabilities of the stage sum
+    // past kStageSumCap or are not finite (the first stage, while m_run is
+    // -inf; masked keys then give NaN): then m_run becomes the maximum so
+    // far, O and l (which hold stages up to j-1, relative to the old
+    // reference) are scaled by alpha, and the stage's probabilities are
+    // formed again. So the row maximum is searched only on those rare stages
+    // and every probability kept is at most 2^13; numerator and denominator
+    // share the reference, so a stale one is exact algebra.
     // Probabilities go to bf16 in pairs; the row sum adds those same bf16
     // values (v_dot2 against 1.0), so numerator and denominator of O use
     // identical weights.
-    const float neg_m = -m_run;
+    float neg_m = -m_run;
     const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
     float psum0 = 0.0f, psum1 = 0.0f;
     constexpr int NP = KT * 8;          // probability pairs per lane and stage
     constexpr int NPV = KS * DT;        // PV MFMAs per stage
     static_assert(NP % NPV == 0, "pairs per PV step");
+    auto exp_pair = [&](int q) -> uint32_t {
+      const int t = q >> 3, a = 2 * (q & 7);
+      const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[t][a], scale_log2, neg_m));
+      const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[t][a + 1], scale_log2, neg_m));
+      const bf16x2 two = __builtin_convertvector((f32x2){p0, p1}, bf16x2);
+      if ((a >> 1) & 1) psum1 = __builtin_amdgcn_fdot2_f32_bf16(two, ones, psum1, false);
+      else psum0 = __builtin_amdgcn_fdot2_f32_bf16(two, ones, psum0, false);
+      const uint32_t bits = bitcast<uint32_t>(two);
+      pk_cur[2 * t + (a >> 3)][(a & 7) >> 1] = bits;
+      return bits;
+    };
     auto exp_pairs = [&](int idx) {     // pairs [idx, idx+1) * NP/NPV
 #pragma unroll
       for (int q = idx * (NP / NPV); q < (idx + 1) * (NP / NPV); ++q) {
-        const int t = q >> 3, a = 2 * (q & 7);
-        const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[t][a], scale_log2, neg_m));
-        const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[t][a + 1], scale_log2, neg_m));
-        const bf16x2 two = __builtin_convertvector((f32x2){p0, p1}, bf16x2);
-        if ((a >> 1) & 1) psum1 = __builtin_amdgcn_fdot2_f32_bf16(two, ones, psum1, false);
-        else psum0 = __builtin_amdgcn_fdot2_f32_bf16(two, ones, psum0, false);
-        const uint32_t bits = bitcast<uint32_t>(two);
-        pk_cur[2 * t + (a >> 3)][(a & 7) >> 1] = bits;
+        const uint32_t bits = exp_pair(q);
         // Anchors: the results are first used after the PV product, and the
         // compiler would otherwise sink this work below its MFMAs.
         asm volatile("" :: "v"(bits));
         asm volatile("" : "+v"(psum0), "+v"(psum1));
       }
     };
-    // ---- O^T += V_{j-1}^T P_{j-1}^T, with the exponentials of stage j in between ----
+    // ---- O^T += V_{j-1}^T P_{j-1}^T, with the probabilities of stage j in between ----
     pv_product(svp, pk_prev, exp_pairs);
-    if (moved) {
+    if (__ballot(!(psum0 + psum1 <= kStageSumCap)) != 0) {
+      asm volatile("");   // rare: keep it a branch
+      float mx = -INFINITY;
+#pragma unroll
+      for (int t = 0; t < KT; ++t)
+#pragma unroll
+        for (int a = 0; a < 16; ++a) mx = fmaxf(mx, sacc[t][a]);
+      const float mb = mx * scale_log2;
+      const float m_new = fmaxf(m_run, fmaxf(mb, __shfl_xor(mb, 32)));
+      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);   // 0 while m_run is -inf
+      m_run = m_new;
       l_run *= alpha;
 #pragma unroll
       for (int u = 0; u < DT; ++u)
 #pragma unroll
         for (int a = 0; a < 16; ++a) oacc[u][a] *= alpha;
+      neg_m = -m_run;
+      psum0 = 0.0f;
+      psum1 = 0.0f;
+#pragma unroll
+      for (int q = 0; q < NP; ++q) exp_pair(q);
     }
     l_run += psum0 + psum1;
     c = c_next;
