@@ -28,9 +28,10 @@ using namespace dev;
 
 constexpr int kPrefetch = 4;
 constexpr int kMaxWaves = 8;
-// A reference maximum moves only when a stage's scores pass it by more than
-// this (log2 units), so e <= 2^8 and the squared sums stay far from overflow.
-constexpr float kRescaleThreshold = 8.0f;
+// A lane's 32 terms of a stage may sum to this against the reference maxima
+// before they move, so every term kept is <= 2^13 and the squared sums stay
+// far from overflow.
+constexpr float kStageSumCap = 8192.0f;
 constexpr int kMaxSlots = kMaxWaves * 32;
 
 // Nearest anchor row of r (ties to the smaller anchor).
@@ -183,17 +184,40 @@ __global__ __launch_bounds__(kMaxWaves * 64) void similarity_bf16_kernel(const S
             }
           }
       }
-      float xr = -INFINITY, xa = -INFINITY;
+      // The stage's terms against the current reference maxima, summed apart
+      // and then added to the totals (one fp32 chain over all of a lane's keys
+      // would lose ~sqrt(N/2) ulps). The references move only when some lane's
+      // 32 terms of either stream sum past kStageSumCap or are not finite (the
+      // first stage, while they are -inf; masked keys then give NaN): then the
+      // maxima are searched, the totals rescaled and the stage summed again.
+      float s_lr, s_la, s_d, s_nr, s_na;
+      auto stage_sums = [&]() {
+        s_lr = s_la = s_d = s_nr = s_na = 0.0f;
 #pragma unroll
-      for (int t = 0; t < KT; ++t)
+        for (int t = 0; t < KT; ++t)
 #pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          xr = fmaxf(xr, sr[t][e]);
-          xa = fmaxf(xa, sa[t][e]);
-        }
-      const float br = xr * scale_log2, ba = xa * scale_log2;
-      if (__ballot(br > m_r + kRescaleThreshold || ba > m_a + kRescaleThreshold) != 0) {
+          for (int e = 0; e < 16; ++e) {
+            const float er = __builtin_amdgcn_exp2f(__builtin_fmaf(sr[t][e], scale_log2, -m_r));
+            const float ea = __builtin_amdgcn_exp2f(__builtin_fmaf(sa[t][e], scale_log2, -m_a));
+            s_lr += er;
+            s_la += ea;
+            s_d = __builtin_fmaf(er, ea, s_d);
+            s_nr = __builtin_fmaf(er, er, s_nr);
+            s_na = __builtin_fmaf(ea, ea, s_na);
+          }
+      };
+      stage_sums();
+      if (__ballot(!(s_lr <= kStageSumCap) || !(s_la <= kStageSumCap)) != 0) {
         asm volatile("");   // rare: keep it a branch
+        float xr = -INFINITY, xa = -INFINITY;
+#pragma unroll
+        for (int t = 0; t < KT; ++t)
+#pragma unroll
+          for (int e = 0; e < 16; ++e) {
+            xr = fmaxf(xr, sr[t][e]);
+            xa = fmaxf(xa, sa[t][e]);
+          }
+        const float br = xr * scale_log2, ba = xa * scale_log2;
         const float nm_r = fmaxf(m_r, fmaxf(br, __shfl_xor(br, 32)));
         const float nm_a = fmaxf(m_a, fmaxf(ba, __shfl_xor(ba, 32)));
         const float fr = __builtin_amdgcn_exp2f(m_r - nm_r);   // 0 while m is -inf
@@ -205,22 +229,8 @@ __global__ __launch_bounds__(kMaxWaves * 64) void similarity_bf16_kernel(const S
         na2 *= fa * fa;
         m_r = nm_r;
         m_a = nm_a;
+        stage_sums();
       }
-      // the stage's terms are summed apart and then added to the totals: one
-      // fp32 chain over all of a lane's keys would lose ~sqrt(N/2) ulps
-      float s_lr = 0.0f, s_la = 0.0f, s_d = 0.0f, s_nr = 0.0f, s_na = 0.0f;
-#pragma unroll
-      for (int t = 0; t < KT; ++t)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          const float er = __builtin_amdgcn_exp2f(__builtin_fmaf(sr[t][e], scale_log2, -m_r));
-          const float ea = __builtin_amdgcn_exp2f(__builtin_fmaf(sa[t][e], scale_log2, -m_a));
-          s_lr += er;
-          s_la += ea;
-          s_d = __builtin_fmaf(er, ea, s_d);
-          s_nr = __builtin_fmaf(er, er, s_nr);
-          s_na = __builtin_fmaf(ea, ea, s_na);
-        }
       l_r += s_lr;
       l_a += s_la;
       dot += s_d;
