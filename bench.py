@@ -502,7 +502,7 @@ def main():
                                       sl.order, stream)
         if ev_pair is not None:
             cal.calibatt_set_kernel_events(ev_pair[0].cuda_event, ev_pair[1].cuda_event)
-        cal.calibatt_layer_dispatch(q, k, v, o, lse, sl, 0, 0, wl.rep_flags, cfg.F, cfg.R, cfg.C, wl.anchors,
+        cal.calibatt_layer_dispatch(q, k, v, o, None, sl, 0, 0, wl.rep_flags, cfg.F, cfg.R, cfg.C, wl.anchors,
                                     scale=wl.scale, stream=stream)
 
     for _ in range(args.warmup):
@@ -528,11 +528,19 @@ def main():
     e0.record(stream)
     reps = max(3, args.steps // 2)
     for _ in range(reps):
-        cal.calibatt_layer_dispatch(q, k, v, o, lse, sl, 0, 0, wl.rep_flags, cfg.F, cfg.R, cfg.C, wl.anchors,
+        cal.calibatt_layer_dispatch(q, k, v, o, None, sl, 0, 0, wl.rep_flags, cfg.F, cfg.R, cfg.C, wl.anchors,
                                     scale=wl.scale, stream=stream)
     e1.record(stream)
     torch.cuda.synchronize()
     layer_ms = e0.elapsed_time(e1) / reps
+    # the same layer-call also writing the optional log-sum-exp (an extra fp32 row sum in the kernel)
+    e0.record(stream)
+    for _ in range(reps):
+        cal.calibatt_layer_dispatch(q, k, v, o, lse, sl, 0, 0, wl.rep_flags, cfg.F, cfg.R, cfg.C, wl.anchors,
+                                    scale=wl.scale, stream=stream)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    layer_lse_ms = e0.elapsed_time(e1) / reps
 
     # layer-call timing protocol: 5 warm-ups, then R calls timed one by one with HIP events, back to
     # back (warm) and with 1 GiB written before each call (cold: more than the 256 MB MALL); the
@@ -542,7 +550,7 @@ def main():
         flush = torch.empty(1 << 28, dtype=torch.float32, device=dev)
 
         def dispatch():
-            cal.calibatt_layer_dispatch(q, k, v, o, lse, sl, 0, 0, wl.rep_flags, cfg.F, cfg.R, cfg.C, wl.anchors,
+            cal.calibatt_layer_dispatch(q, k, v, o, None, sl, 0, 0, wl.rep_flags, cfg.F, cfg.R, cfg.C, wl.anchors,
                                         scale=wl.scale, stream=stream)
 
         def timed(cold):
@@ -580,11 +588,11 @@ def main():
                                        stream)
     torch.cuda.synchronize()
     compile_iv_ms = (time.perf_counter() - t_c) * 1e3 / 5
-    cal.calibatt_layer_dispatch_iv(q, k, v, o, lse, il, 0, 0, wl.rep_flags, cfg.F, cfg.R, cfg.C, wl.anchors,
+    cal.calibatt_layer_dispatch_iv(q, k, v, o, None, il, 0, 0, wl.rep_flags, cfg.F, cfg.R, cfg.C, wl.anchors,
                                    scale=wl.scale, stream=stream)
     e0.record(stream)
     for _ in range(reps):
-        cal.calibatt_layer_dispatch_iv(q, k, v, o, lse, il, 0, 0, wl.rep_flags, cfg.F, cfg.R, cfg.C, wl.anchors,
+        cal.calibatt_layer_dispatch_iv(q, k, v, o, None, il, 0, 0, wl.rep_flags, cfg.F, cfg.R, cfg.C, wl.anchors,
                                        scale=wl.scale, stream=stream)
     e1.record(stream)
     torch.cuda.synchronize()
@@ -640,7 +648,7 @@ def main():
         "config": {"workload": f"{cfg.key}: {cfg.title}", "H": cfg.H, "N": cfg.N, "d": cfg.d, "B": cfg.B,
                    "frames_rows_cols": [cfg.F, cfg.R, cfg.C], "sparse_heads": len(work["sparse_heads"]),
                    "repetitive_heads": len(work["rep_heads"]), "anchor_rows": [int(a) for a in wl.anchors],
-                   "step": "calibatt_compile_skiplist + calibatt_layer_dispatch"},
+                   "step": "calibatt_compile_skiplist + calibatt_layer_dispatch (O; lse timed separately)"},
         "pct_of_bf16_peak": round(100.0 * value / PEAK_BF16_TFLOPS, 2),
         "layer_call_ms": round(layer_ms, 3),
         "compile_ms": round(compile_ms, 3),
@@ -651,6 +659,7 @@ def main():
         "dense_same_kernel_ms": round(dense_ms, 3) if dense_ms else None,
         "dense_tflops": round(work["flops_dense"] / (dense_ms * 1e-3) / 1e12, 1) if dense_ms else None,
         "speedup_vs_dense": round(dense_ms / layer_ms, 3) if dense_ms else None,
+        "layer_call_with_lse_ms": round(layer_lse_ms, 3),
         "layer_call_protocol": protocol,
         "intervals": intervals,
         "sparsity": {"token_sparse_heads": work["token_sparsity_sparse_heads"],

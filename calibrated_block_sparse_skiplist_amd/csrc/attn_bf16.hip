@@ -102,7 +102,12 @@ __device__ __forceinline__ int query_token(const AttnParams& p, const Item& it, 
   return (f * p.R + p.anchors[ai]) * p.C + c;
 }
 
-template <int D, int BLK>
+// LSE: the log-sum-exp output is requested (p.lse). O is normalised by the
+// sum of the bf16 probabilities that also enter the PV product, so numerator
+// and denominator share their rounding; that sum can be 2^-8 off the true row
+// sum when a few rounded terms dominate a row, so lse takes a second, fp32 sum
+// of the probabilities, kept only in this instantiation.
+template <int D, int BLK, bool LSE>
 __global__ __launch_bounds__(BLK * 2) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void attn_bf16_kernel(const AttnParams p) {
   constexpr int NW = BLK / 32;           // waves per workgroup (32 queries each)
@@ -234,7 +239,8 @@ void attn_bf16_kernel(const AttnParams p) {
 #pragma unroll
   for (int u = 0; u < DT; ++u) oacc[u] = f32x16{};
   float m_run = -INFINITY;   // reference maximum of scaled scores (log2 units)
-  float l_run = 0.0f;        // this lane's partial sum of probabilities
+  float l_run = 0.0f;        // this lane's partial sum of probabilities (bf16-rounded, as in PV)
+  float lf_run = 0.0f;       // the same sum in fp32 (lse only)
 
   // Software pipeline over 64-key stages. Stage j computes S^T_j and its
   // probabilities P_j, while the matrix pipe runs the PV product of stage
@@ -412,6 +418,7 @@ void attn_bf16_kernel(const AttnParams p) {
     float neg_m = -m_run;
     const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
     float psum0 = 0.0f, psum1 = 0.0f;
+    float f32sum0 = 0.0f, f32sum1 = 0.0f;   // (LSE only)
     constexpr int NP = KT * 8;          // probability pairs per lane and stage
     constexpr int NPV = KS * DT;        // PV MFMAs per stage
     static_assert(NP % NPV == 0, "pairs per PV step");
@@ -422,6 +429,10 @@ void attn_bf16_kernel(const AttnParams p) {
       const bf16x2 two = __builtin_convertvector((f32x2){p0, p1}, bf16x2);
       if ((a >> 1) & 1) psum1 = __builtin_amdgcn_fdot2_f32_bf16(two, ones, psum1, false);
       else psum0 = __builtin_amdgcn_fdot2_f32_bf16(two, ones, psum0, false);
+      if constexpr (LSE) {
+        f32sum0 += p0;
+        f32sum1 += p1;
+      }
       const uint32_t bits = bitcast<uint32_t>(two);
       pk_cur[2 * t + (a >> 3)][(a & 7) >> 1] = bits;
       return bits;
@@ -434,6 +445,7 @@ void attn_bf16_kernel(const AttnParams p) {
         // compiler would otherwise sink this work below its MFMAs.
         asm volatile("" :: "v"(bits));
         asm volatile("" : "+v"(psum0), "+v"(psum1));
+        if constexpr (LSE) asm volatile("" : "+v"(f32sum0), "+v"(f32sum1));
       }
     };
     // ---- O^T += V_{j-1}^T P_{j-1}^T, with the probabilities of stage j in between ----
@@ -450,6 +462,7 @@ void attn_bf16_kernel(const AttnParams p) {
       const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);   // 0 while m_run is -inf
       m_run = m_new;
       l_run *= alpha;
+      lf_run *= alpha;
 #pragma unroll
       for (int u = 0; u < DT; ++u)
 #pragma unroll
@@ -457,10 +470,13 @@ void attn_bf16_kernel(const AttnParams p) {
       neg_m = -m_run;
       psum0 = 0.0f;
       psum1 = 0.0f;
+      f32sum0 = 0.0f;
+      f32sum1 = 0.0f;
 #pragma unroll
       for (int q = 0; q < NP; ++q) exp_pair(q);
     }
     l_run += psum0 + psum1;
+    if constexpr (LSE) lf_run += f32sum0 + f32sum1;
     c = c_next;
   };
   for (int j = 0; j < n_stages; j += 2) {
@@ -477,6 +493,8 @@ void attn_bf16_kernel(const AttnParams p) {
 
   // ---- epilogue ----
   const float l_tot = l_run + __shfl_xor(l_run, 32);
+  float lf_tot = 0.0f;
+  if constexpr (LSE) lf_tot = lf_run + __shfl_xor(lf_run, 32);
   const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
   if (qtok >= 0) {
     u16* O = static_cast<u16*>(p.o) + (int64_t)it.head * p.head_stride + (int64_t)qtok * D;
@@ -491,8 +509,9 @@ void attn_bf16_kernel(const AttnParams p) {
             (f32x2){oacc[u][4 * g4 + 2] * inv, oacc[u][4 * g4 + 3] * inv}, bf16x2);
         *reinterpret_cast<uint2*>(O + d0) = make_uint2(bitcast<uint32_t>(v01), bitcast<uint32_t>(v23));
       }
-    if (p.lse && h == 0) {
-      p.lse[(int64_t)it.head * n_tok + qtok] = l_tot > 0.0f ? (m_run + __log2f(l_tot)) * kLn2 : -INFINITY;
+    if constexpr (LSE) {
+      if (h == 0)
+        p.lse[(int64_t)it.head * n_tok + qtok] = lf_tot > 0.0f ? (m_run + __log2f(lf_tot)) * kLn2 : -INFINITY;
     }
   }
 }
@@ -501,7 +520,8 @@ template <int D, int BLK>
 hipError_t launch_typed(const AttnParams& p, hipStream_t s) {
   const int64_t items = attn_items(p);
   if (items == 0) return hipSuccess;
-  hipLaunchKernelGGL((attn_bf16_kernel<D, BLK>), dim3((unsigned)items), dim3(BLK * 2), 0, s, p);
+  if (p.lse) hipLaunchKernelGGL((attn_bf16_kernel<D, BLK, true>), dim3((unsigned)items), dim3(BLK * 2), 0, s, p);
+  else hipLaunchKernelGGL((attn_bf16_kernel<D, BLK, false>), dim3((unsigned)items), dim3(BLK * 2), 0, s, p);
   return hipGetLastError();
 }
 
