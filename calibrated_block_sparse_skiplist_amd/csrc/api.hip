@@ -235,11 +235,12 @@ calibatt_status_t compile_impl(const uint8_t* masks, int32_t T, int32_t L, int32
   if (capacity < total)
     return fail(CALIBATT_ERR_CAPACITY, "the output holds %lld entries, %lld needed", (long long)capacity,
                 (long long)total);
-  e = runs ? calibatt::launch_compile_runs_fill(masks, rows, (int)nb, ptr, static_cast<uint32_t*>(out), s)
+  // (the interval fill leaves each row's kept count in order for the ranking)
+  e = runs ? calibatt::launch_compile_runs_fill(masks, rows, (int)nb, ptr, static_cast<uint32_t*>(out), order, s)
            : calibatt::launch_compile_fill(masks, rows, (int)nb, ptr, static_cast<int32_t*>(out), s);
   if (e != hipSuccess) return hip_fail(e, "skip-list fill kernel launch");
   if (order) {
-    e = runs ? calibatt::launch_compile_runs_order(ptr, static_cast<const uint32_t*>(out), records, (int)nb, order, s)
+    e = runs ? calibatt::launch_compile_runs_order(records, (int)nb, order, s)
              : calibatt::launch_compile_order(ptr, records, (int)nb, order, s);
     if (e != hipSuccess) return hip_fail(e, "skip-list order kernel launch");
   }

@@ -131,8 +131,7 @@ hipError_t launch_compile_order(const int64_t* row_ptr, int64_t records, int nb,
 hipError_t launch_compile_runs_count_scan(const uint8_t* masks, int64_t rows, int nb, int64_t* iv_ptr,
                                           hipStream_t s);
 hipError_t launch_compile_runs_fill(const uint8_t* masks, int64_t rows, int nb, const int64_t* iv_ptr,
-                                    uint32_t* iv, hipStream_t s);
-hipError_t launch_compile_runs_order(const int64_t* iv_ptr, const uint32_t* iv, int64_t records, int nb,
-                                     int32_t* order, hipStream_t s);
+                                    uint32_t* iv, int32_t* kept_out, hipStream_t s);
+hipError_t launch_compile_runs_order(int64_t records, int nb, int32_t* order, hipStream_t s);
 
 }  // namespace calibatt

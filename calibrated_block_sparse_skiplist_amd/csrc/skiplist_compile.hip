@@ -7,7 +7,7 @@
 // flattened (record, query block) pairs; lists are ascending.
 //
 // Passes (all integer work, so results are exact):
-//   1. count: one wave per mask row counts nonzero bytes with ballots into
+//   1. count: one wave per mask row counts its nonzero bytes into
 //      row_ptr[1 + row]; segment_scan then scans each segment of kSeg rows in place.
 //   2. scan_totals: one workgroup turns the segment-end values into a global
 //      inclusive scan.
@@ -17,10 +17,14 @@
 //   5. order: one workgroup per record ranks query blocks by (-count, index).
 // The interval form (one [lo, hi) pair per maximal run of kept blocks: the
 // contiguous key-block intervals of the same Key Design 4) reuses the scan:
-// run_count counts run openings, run_fill writes each run's two ends, and
-// run_order sums a row's run lengths for the same ranking.
-// Mask bytes are read once in pass 1 and once in pass 4; every pass reads its
-// rows with lanes on consecutive bytes so the loads coalesce.
+// run_count counts run openings, run_fill writes each run's two ends (and,
+// for the ranking, each row's kept count into the order array), and
+// run_order ranks those counts in place.
+// Mask bytes are read once in pass 1 and once in pass 4. A wave reads a row
+// as 16-byte aligned chunks, one per lane (1 KB per load instruction), and
+// turns each chunk into 16 "kept" bits with a few integer operations; waves
+// stride over the rows. Outputs go through a small LDS buffer per wave so the
+// stores are contiguous.
 #include "internal.h"
 
 namespace calibatt {
@@ -29,14 +33,59 @@ namespace {
 constexpr int kSeg = 1024;        // rows per scan segment
 constexpr int kThreads = 256;     // threads per workgroup
 
-__device__ inline int row_count(const uint8_t* row, int nb, int lane) {
-  int cnt = 0;
-  for (int base = 0; base < nb; base += 64) {
-    int c = base + lane;
-    bool nz = c < nb && row[c] != 0;
-    cnt += __popcll(__ballot(nz));
+constexpr int kWaves = kThreads / 64;   // waves per workgroup
+constexpr int kWin = 64 * 16;           // mask bytes one wave load covers
+
+// Bits 0..3: which bytes of x are nonzero (bit 7 of each byte of
+// ((x & 0x7f..) + 0x7f..) | x is set exactly for the nonzero bytes).
+__device__ __forceinline__ uint32_t nonzero_bytes(uint32_t x) {
+  const uint32_t y = (((x & 0x7F7F7F7Fu) + 0x7F7F7F7Fu) | x) >> 7 & 0x01010101u;
+  return (y | (y >> 7) | (y >> 14) | (y >> 21)) & 0xFu;
+}
+
+// Row r of the masks is the byte span [s, e) = [r*nb, r*nb + nb). cs0 is the
+// offset of the first 16-byte aligned chunk (in memory) that meets it; mis =
+// address of the masks modulo 16.
+struct RowSpan {
+  int64_t s, e, cs0;
+};
+__device__ __forceinline__ RowSpan row_span(int64_t row, int nb, int mis) {
+  const int64_t s = row * nb;
+  return {s, s + nb, ((s + mis) & ~(int64_t)15) - mis};
+}
+
+// Kept bits of the chunk at byte offset cs (16-byte aligned in memory): bit j
+// is set when byte cs + j lies in [s, e) and is nonzero. A chunk that would
+// reach outside the masks [0, total) reads only its bytes inside the row.
+__device__ __forceinline__ uint32_t chunk_bits(const uint8_t* masks, int64_t total, int64_t s, int64_t e,
+                                               int64_t cs) {
+  const int64_t lo = s > cs ? s - cs : 0;
+  const int64_t hi = e - cs < 16 ? e - cs : 16;
+  if (hi <= lo) return 0u;
+  uint32_t bits = 0u;
+  if (cs >= 0 && cs + 16 <= total) {
+    const uint4 x = *reinterpret_cast<const uint4*>(masks + cs);
+    bits = nonzero_bytes(x.x) | (nonzero_bytes(x.y) << 4) | (nonzero_bytes(x.z) << 8) | (nonzero_bytes(x.w) << 12);
+  } else {
+    for (int64_t j = lo; j < hi; ++j) bits |= (masks[cs + j] != 0 ? 1u : 0u) << j;
   }
-  return cnt;
+  return bits & (0xFFFFu >> (16 - (int)hi)) & (0xFFFFu << (int)lo);
+}
+
+__device__ __forceinline__ int wave_sum(int v) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off);
+  return v;
+}
+
+// Inclusive prefix sum over the 64 lanes.
+__device__ __forceinline__ int wave_inclusive_scan(int v, int lane) {
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int t = __shfl_up(v, off);
+    if (lane >= off) v += t;
+  }
+  return v;
 }
 
 // Inclusive scan of n <= kSeg int64 values in LDS by kThreads threads.
@@ -66,15 +115,34 @@ __device__ void block_inclusive_scan(int64_t* vals, int n, int64_t* partial) {
   __syncthreads();
 }
 
-// One wave per mask row: row_ptr[1 + row] = number of nonzero bytes.
+// row_ptr[1 + row] = number of nonzero bytes of the row; waves stride over
+// rows two at a time (both rows' loads in flight together).
 __global__ __launch_bounds__(kThreads) void count_kernel(const uint8_t* __restrict__ masks, int64_t rows, int nb,
                                                          int64_t* __restrict__ row_ptr) {
   const int lane = threadIdx.x & 63;
-  const int64_t row = (int64_t)blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6);
-  if (row >= rows) return;
-  const int cnt = row_count(masks + row * nb, nb, lane);
-  if (lane == 0) row_ptr[1 + row] = cnt;
-  if (row == 0 && lane == 0) row_ptr[0] = 0;
+  const int mis = (int)((uintptr_t)masks & 15);
+  const int64_t total = rows * nb;
+  const int64_t stride = (int64_t)gridDim.x * kWaves;
+  for (int64_t ra = (int64_t)blockIdx.x * kWaves + (threadIdx.x >> 6); ra < rows; ra += 2 * stride) {
+    const int64_t rb = ra + stride;
+    const RowSpan a = row_span(ra, nb, mis);
+    const RowSpan b = row_span(rb < rows ? rb : ra, nb, mis);
+    int ca = 0, cb = 0;
+    // (the two rows may need different window counts: their alignment slack differs)
+    for (int64_t w = 0; a.cs0 + w < a.e || b.cs0 + w < b.e; w += kWin) {
+      const uint32_t ba = chunk_bits(masks, total, a.s, a.e, a.cs0 + w + 16 * lane);
+      const uint32_t bb = chunk_bits(masks, total, b.s, b.e, b.cs0 + w + 16 * lane);
+      ca += __popc(ba);
+      cb += __popc(bb);
+    }
+    ca = wave_sum(ca);
+    cb = wave_sum(cb);
+    if (lane == 0) {
+      row_ptr[1 + ra] = ca;
+      if (rb < rows) row_ptr[1 + rb] = cb;
+    }
+  }
+  if (blockIdx.x == 0 && threadIdx.x == 0) row_ptr[0] = 0;
 }
 
 // In-place inclusive scan of each segment of kSeg counts.
@@ -119,21 +187,36 @@ __global__ __launch_bounds__(kThreads) void add_offsets_kernel(int64_t rows, int
   for (int i = threadIdx.x; i < n - 1; i += kThreads) row_ptr[1 + row0 + i] += offset;
 }
 
+// col_idx[row_ptr[row] ..] = the row's nonzero byte positions, ascending.
+// Per 1 KB window a wave places its indices in LDS (each lane after the
+// lanes before it) and then stores them contiguously.
 __global__ __launch_bounds__(kThreads) void fill_kernel(const uint8_t* __restrict__ masks, int64_t rows,
                                                         int nb, const int64_t* __restrict__ row_ptr,
                                                         int32_t* __restrict__ col_idx) {
+  __shared__ int32_t stage[kWaves][kWin];
   const int lane = threadIdx.x & 63;
-  const int64_t row = (int64_t)blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6);
-  if (row >= rows) return;
-  const uint8_t* m = masks + row * nb;
-  int64_t out = row_ptr[row];
-  const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-  for (int base = 0; base < nb; base += 64) {
-    int c = base + lane;
-    bool nz = c < nb && m[c] != 0;
-    uint64_t bal = __ballot(nz);
-    if (nz) col_idx[out + __popcll(bal & below)] = c;
-    out += __popcll(bal);
+  int32_t* const buf = stage[threadIdx.x >> 6];
+  const int mis = (int)((uintptr_t)masks & 15);
+  const int64_t total = rows * nb;
+  const int64_t stride = (int64_t)gridDim.x * kWaves;
+  for (int64_t row = (int64_t)blockIdx.x * kWaves + (threadIdx.x >> 6); row < rows; row += stride) {
+    const RowSpan r = row_span(row, nb, mis);
+    int64_t out = row_ptr[row];
+    for (int64_t w = r.cs0; w < r.e; w += kWin) {
+      const int64_t cs = w + 16 * lane;
+      const uint32_t bits = chunk_bits(masks, total, r.s, r.e, cs);
+      const int n = __popc(bits);
+      const int incl = wave_inclusive_scan(n, lane);
+      const int n_win = __shfl(incl, 63);
+      const int c0 = (int)(cs - r.s);        // column of bit 0 (bits before the row are clear)
+      int pos = incl - n;
+#pragma unroll
+      for (int j = 0; j < 16; ++j)
+        if ((bits >> j) & 1u) buf[pos++] = c0 + j;
+      // (one wave: its LDS writes above complete before these reads)
+      for (int i = lane; i < n_win; i += 64) col_idx[out + i] = buf[i];
+      out += n_win;
+    }
   }
 }
 
@@ -161,60 +244,93 @@ __global__ __launch_bounds__(kThreads) void order_kernel(const int64_t* __restri
 // closes a run when it is kept and block c+1 is not (or c = nb-1). The k-th
 // opening and the k-th closing of a row belong to the same run.
 
-// Kept bit of block c of a row, false outside [0, nb).
-__device__ inline bool kept(const uint8_t* row, int nb, int c) { return c >= 0 && c < nb && row[c] != 0; }
-
-// One wave per mask row: iv_ptr[1 + row] = number of runs.
+// iv_ptr[1 + row] = number of runs of the row (kept bytes whose left
+// neighbour is not kept; the last byte of the previous window is carried).
 __global__ __launch_bounds__(kThreads) void run_count_kernel(const uint8_t* __restrict__ masks, int64_t rows,
                                                              int nb, int64_t* __restrict__ iv_ptr) {
   const int lane = threadIdx.x & 63;
-  const int64_t row = (int64_t)blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6);
-  if (row >= rows) return;
-  const uint8_t* m = masks + row * nb;
-  int cnt = 0;
-  for (int base = 0; base < nb; base += 64) {
-    const int c = base + lane;
-    cnt += __popcll(__ballot(kept(m, nb, c) && !kept(m, nb, c - 1)));
+  const int mis = (int)((uintptr_t)masks & 15);
+  const int64_t total = rows * nb;
+  const int64_t stride = (int64_t)gridDim.x * kWaves;
+  for (int64_t row = (int64_t)blockIdx.x * kWaves + (threadIdx.x >> 6); row < rows; row += stride) {
+    const RowSpan r = row_span(row, nb, mis);
+    uint32_t carry = 0u;
+    int cnt = 0;
+    for (int64_t w = r.cs0; w < r.e; w += kWin) {
+      const uint32_t bits = chunk_bits(masks, total, r.s, r.e, w + 16 * lane);
+      uint32_t prev = (__shfl_up(bits, 1) >> 15) & 1u;   // last byte of the lane before
+      if (lane == 0) prev = carry;
+      cnt += __popc(bits & ~((bits << 1) | prev));
+      carry = (__shfl(bits, 63) >> 15) & 1u;
+    }
+    cnt = wave_sum(cnt);
+    if (lane == 0) iv_ptr[1 + row] = cnt;
   }
-  if (lane == 0) iv_ptr[1 + row] = cnt;
-  if (row == 0 && lane == 0) iv_ptr[0] = 0;
+  if (blockIdx.x == 0 && threadIdx.x == 0) iv_ptr[0] = 0;
 }
 
-// One wave per mask row: writes lo into the low and hi into the high 16 bits
-// of each packed run (little-endian halves of the uint32 entry).
+// The row's runs, lo in the low and hi in the high 16 bits of each entry: the
+// k-th opening (kept byte, left neighbour not kept) gives lo of run k, the
+// k-th closing (kept byte, right neighbour not kept) gives hi = position + 1.
+// A run may span windows, so the row's runs are assembled in LDS (runs_cap =
+// ceil(nb/2) entries per wave, dynamic) and stored contiguously at the end.
+// kept_out (nullable) receives each row's kept-block count for run_order.
 __global__ __launch_bounds__(kThreads) void run_fill_kernel(const uint8_t* __restrict__ masks, int64_t rows,
                                                             int nb, const int64_t* __restrict__ iv_ptr,
-                                                            uint16_t* __restrict__ iv16) {
+                                                            uint32_t* __restrict__ iv, int runs_cap,
+                                                            int32_t* __restrict__ kept_out) {
+  extern __shared__ uint32_t run_stage[];
   const int lane = threadIdx.x & 63;
-  const int64_t row = (int64_t)blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6);
-  if (row >= rows) return;
-  const uint8_t* m = masks + row * nb;
-  int64_t n_open = iv_ptr[row], n_close = iv_ptr[row];
-  const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-  for (int base = 0; base < nb; base += 64) {
-    const int c = base + lane;
-    const bool here = kept(m, nb, c);
-    const bool opens = here && !kept(m, nb, c - 1);
-    const bool closes = here && !kept(m, nb, c + 1);
-    const uint64_t bo = __ballot(opens), bc = __ballot(closes);
-    if (opens) iv16[2 * (n_open + __popcll(bo & below))] = (uint16_t)c;
-    if (closes) iv16[2 * (n_close + __popcll(bc & below)) + 1] = (uint16_t)(c + 1);
-    n_open += __popcll(bo);
-    n_close += __popcll(bc);
+  uint32_t* const buf = run_stage + (threadIdx.x >> 6) * runs_cap;
+  uint16_t* const half = reinterpret_cast<uint16_t*>(buf);
+  const int mis = (int)((uintptr_t)masks & 15);
+  const int64_t total = rows * nb;
+  const int64_t stride = (int64_t)gridDim.x * kWaves;
+  for (int64_t row = (int64_t)blockIdx.x * kWaves + (threadIdx.x >> 6); row < rows; row += stride) {
+    const RowSpan r = row_span(row, nb, mis);
+    uint32_t carry = 0u;
+    int n_open = 0, n_close = 0, n_kept = 0;
+    for (int64_t w = r.cs0; w < r.e; w += kWin) {
+      const int64_t cs = w + 16 * lane;
+      const uint32_t bits = chunk_bits(masks, total, r.s, r.e, cs);
+      n_kept += __popc(bits);
+      uint32_t prev = (__shfl_up(bits, 1) >> 15) & 1u;
+      if (lane == 0) prev = carry;
+      uint32_t next = __shfl_down(bits, 1) & 1u;   // first byte of the lane after
+      if (lane == 63) {                             // first byte of the next window, if in the row
+        const int64_t nx = cs + 16;
+        next = (nx >= r.s && nx < r.e && masks[nx] != 0) ? 1u : 0u;
+      }
+      const uint32_t opens = bits & ~((bits << 1) | prev);
+      const uint32_t closes = bits & ~((bits >> 1) | (next << 15));
+      const int no = __popc(opens), nc = __popc(closes);
+      const int io = wave_inclusive_scan(no, lane), ic = wave_inclusive_scan(nc, lane);
+      const int c0 = (int)(cs - r.s);
+      int ko = n_open + io - no, kc = n_close + ic - nc;
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        if ((opens >> j) & 1u) half[2 * ko++] = (uint16_t)(c0 + j);
+        if ((closes >> j) & 1u) half[2 * kc++ + 1] = (uint16_t)(c0 + j + 1);
+      }
+      n_open += __shfl(io, 63);
+      n_close += __shfl(ic, 63);
+      carry = (__shfl(bits, 63) >> 15) & 1u;
+    }
+    const int64_t base = iv_ptr[row];
+    for (int i = lane; i < n_open; i += 64) iv[base + i] = buf[i];
+    if (kept_out) {
+      n_kept = wave_sum(n_kept);
+      if (lane == 0) kept_out[row] = n_kept;
+    }
   }
 }
 
-// Same ranking as order_kernel, with each row's kept count summed over its runs.
-__global__ __launch_bounds__(kThreads) void run_order_kernel(const int64_t* __restrict__ iv_ptr,
-                                                             const uint32_t* __restrict__ iv, int nb,
-                                                             int32_t* __restrict__ order) {
+// Same ranking as order_kernel; each row's kept count was left in order[]
+// by run_fill, and is read into LDS before the ranks overwrite it.
+__global__ __launch_bounds__(kThreads) void run_order_kernel(int nb, int32_t* __restrict__ order) {
   extern __shared__ int32_t cnt[];
   const int64_t row0 = (int64_t)blockIdx.x * nb;
-  for (int r = threadIdx.x; r < nb; r += kThreads) {
-    int c = 0;
-    for (int64_t i = iv_ptr[row0 + r]; i < iv_ptr[row0 + r + 1]; ++i) c += (int)(iv[i] >> 16) - (int)(iv[i] & 0xffffu);
-    cnt[r] = c;
-  }
+  for (int r = threadIdx.x; r < nb; r += kThreads) cnt[r] = order[row0 + r];
   __syncthreads();
   for (int r = threadIdx.x; r < nb; r += kThreads) {
     const int c = cnt[r];
@@ -245,10 +361,17 @@ hipError_t scan_counts(int64_t rows, int64_t* row_ptr, hipStream_t s) {
 
 }  // namespace
 
+// Workgroups of the row-striding kernels: enough waves to keep every CU's
+// loads in flight, no more than the rows need.
+unsigned stride_grid(int64_t rows) {
+  const int64_t need = (rows + kWaves - 1) / kWaves;
+  return (unsigned)(need < 4096 ? need : 4096);
+}
+
 hipError_t launch_compile_count_scan(const uint8_t* masks, int64_t rows, int nb, int64_t* row_ptr,
                                      hipStream_t s) {
-  const int64_t grid = (rows + kThreads / 64 - 1) / (kThreads / 64);
-  hipLaunchKernelGGL(count_kernel, dim3((unsigned)grid), dim3(kThreads), 0, s, masks, rows, nb, row_ptr);
+  const unsigned grid = stride_grid(rows);
+  hipLaunchKernelGGL(count_kernel, dim3(grid), dim3(kThreads), 0, s, masks, rows, nb, row_ptr);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   return scan_counts(rows, row_ptr, s);
@@ -256,8 +379,8 @@ hipError_t launch_compile_count_scan(const uint8_t* masks, int64_t rows, int nb,
 
 hipError_t launch_compile_fill(const uint8_t* masks, int64_t rows, int nb, const int64_t* row_ptr,
                                int32_t* col_idx, hipStream_t s) {
-  const int64_t grid = (rows + kThreads / 64 - 1) / (kThreads / 64);
-  hipLaunchKernelGGL(fill_kernel, dim3((unsigned)grid), dim3(kThreads), 0, s, masks, rows, nb, row_ptr, col_idx);
+  const unsigned grid = stride_grid(rows);
+  hipLaunchKernelGGL(fill_kernel, dim3(grid), dim3(kThreads), 0, s, masks, rows, nb, row_ptr, col_idx);
   return hipGetLastError();
 }
 
@@ -270,25 +393,26 @@ hipError_t launch_compile_order(const int64_t* row_ptr, int64_t records, int nb,
 
 hipError_t launch_compile_runs_count_scan(const uint8_t* masks, int64_t rows, int nb, int64_t* iv_ptr,
                                           hipStream_t s) {
-  const int64_t grid = (rows + kThreads / 64 - 1) / (kThreads / 64);
-  hipLaunchKernelGGL(run_count_kernel, dim3((unsigned)grid), dim3(kThreads), 0, s, masks, rows, nb, iv_ptr);
+  const unsigned grid = stride_grid(rows);
+  hipLaunchKernelGGL(run_count_kernel, dim3(grid), dim3(kThreads), 0, s, masks, rows, nb, iv_ptr);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   return scan_counts(rows, iv_ptr, s);
 }
 
 hipError_t launch_compile_runs_fill(const uint8_t* masks, int64_t rows, int nb, const int64_t* iv_ptr,
-                                    uint32_t* iv, hipStream_t s) {
-  const int64_t grid = (rows + kThreads / 64 - 1) / (kThreads / 64);
-  hipLaunchKernelGGL(run_fill_kernel, dim3((unsigned)grid), dim3(kThreads), 0, s, masks, rows, nb, iv_ptr,
-                     reinterpret_cast<uint16_t*>(iv));
+                                    uint32_t* iv, int32_t* kept_out, hipStream_t s) {
+  const unsigned grid = stride_grid(rows);
+  const int runs_cap = (nb + 1) / 2;
+  const size_t lds = (size_t)kWaves * runs_cap * sizeof(uint32_t);
+  hipLaunchKernelGGL(run_fill_kernel, dim3(grid), dim3(kThreads), lds, s, masks, rows, nb, iv_ptr, iv, runs_cap,
+                     kept_out);
   return hipGetLastError();
 }
 
-hipError_t launch_compile_runs_order(const int64_t* iv_ptr, const uint32_t* iv, int64_t records, int nb,
-                                     int32_t* order, hipStream_t s) {
+hipError_t launch_compile_runs_order(int64_t records, int nb, int32_t* order, hipStream_t s) {
   hipLaunchKernelGGL(run_order_kernel, dim3((unsigned)records), dim3(kThreads), (size_t)nb * sizeof(int32_t), s,
-                     iv_ptr, iv, nb, order);
+                     nb, order);
   return hipGetLastError();
 }
 

@@ -65,6 +65,40 @@ def test_runs_across_64_block_windows():
     assert il.n_iv == 8
 
 
+def test_runs_across_1kb_windows():
+    # the compile reads a row 1 KB (1024 blocks) per wave load; runs that start, end or continue at
+    # those window edges, for rows starting at several alignments (nb odd)
+    nb = 2101
+    masks = np.zeros((1, 1, 1, nb, nb), np.uint8)
+    spans = [(1000, 1100), (1023, 1025), (1024, 2048), (0, 2101), (2047, 2049), (5, 1024), (1024, 1025),
+             (2100, 2101), (0, 1), (1020, 2060)]
+    for r, (lo, hi) in enumerate(spans):
+        masks[0, 0, 0, r, lo:hi] = 1
+    masks[0, 0, 0, len(spans), ::2] = 5       # alternating across both window edges
+    il = _compile_and_compare(masks, nb * 16, 16, "1 KB window edges")
+    assert il.n_iv == len(spans) + (nb + 1) // 2
+
+
+@pytest.mark.parametrize("offset", [1, 7, 13])
+@pytest.mark.parametrize("nb", [33, 591, 1030])
+def test_masks_not_16_byte_aligned(offset, nb):
+    """Masks starting at any byte address give the same runs (the compile reads 16-byte aligned chunks)."""
+    rng = np.random.default_rng(offset * 1000 + nb)
+    masks = (rng.random((1, 1, 2, nb, nb)) < 0.6).astype(np.uint8)
+    buf = torch.zeros(masks.size + 64, dtype=torch.uint8, device="cuda")
+    view = buf[offset:offset + masks.size]
+    view.copy_(torch.from_numpy(masks.reshape(-1)).cuda())
+    say(f"[intervals] masks at byte offset {offset} (address % 16 = {view.data_ptr() % 16}), nb={nb}")
+    il = cal.compile_intervals(view.view(masks.shape), nb * 16, 16)
+    torch.cuda.synchronize()
+    ptr, runs, order = oracle.compile_intervals(masks)
+    assert il.n_iv == int(ptr[-1])
+    np.testing.assert_array_equal(il.iv_ptr.cpu().numpy(), ptr)
+    got = il.iv.cpu().numpy()[:il.n_iv].astype(np.int64)
+    np.testing.assert_array_equal(np.stack([got & 0xffff, got >> 16], axis=1), runs)
+    np.testing.assert_array_equal(il.order.cpu().numpy(), order)
+
+
 def test_many_segments_scan():
     masks = _random((2, 4, 5, 300, 300), 0.3, 9)
     _compile_and_compare(masks, 300 * 128 - 50, 128, "multi-segment")

@@ -41,6 +41,25 @@ def test_random_masks(shape, p, seed):
     _compile_and_compare(masks, nb * 16, 16, f"random {shape} p={p}")
 
 
+@pytest.mark.parametrize("offset", [1, 7, 13])
+@pytest.mark.parametrize("nb", [33, 591, 1030])
+def test_masks_not_16_byte_aligned(offset, nb):
+    """The compile reads masks as 16-byte aligned chunks: masks starting at any byte address give the same lists."""
+    rng = np.random.default_rng(offset * 1000 + nb)
+    masks = (rng.random((1, 1, 2, nb, nb)) < 0.4).astype(np.uint8)
+    buf = torch.zeros(masks.size + 64, dtype=torch.uint8, device="cuda")
+    view = buf[offset:offset + masks.size]
+    view.copy_(torch.from_numpy(masks.reshape(-1)).cuda())
+    say(f"[skiplist] masks at byte offset {offset} (address % 16 = {view.data_ptr() % 16}), nb={nb}")
+    sl = cal.compile_skiplist(view.view(masks.shape), nb * 16, 16)
+    torch.cuda.synchronize()
+    rp, ci, order = oracle.compile_skiplist(masks)
+    assert sl.nnz == int(rp[-1])
+    np.testing.assert_array_equal(sl.row_ptr.cpu().numpy(), rp)
+    np.testing.assert_array_equal(sl.col_idx.cpu().numpy()[:sl.nnz], ci)
+    np.testing.assert_array_equal(sl.order.cpu().numpy(), order)
+
+
 def test_all_zero_dictionary_has_no_entries():
     masks = np.zeros((1, 2, 3, 40, 40), np.uint8)
     sl = _compile_and_compare(masks, 40 * 64, 64, "all zero")
