@@ -26,8 +26,9 @@
 //      transpose across 16-lane groups), B = P^T packed to bf16 straight from
 //      the S^T accumulators; the contraction runs over keys in the order the
 //      accumulator layout holds them, and V is read in that same order. The
-//      exponentials of step 2 are issued between these MFMAs, so the matrix
-//      pipe keeps running while the wave computes probabilities.
+//      exponentials of step 2 are issued between these MFMAs and the last
+//      S^T MFMAs of the stage (those of key tile 0 once it is complete), so
+//      the matrix pipe keeps running while the wave computes probabilities.
 // K and V tiles move HBM -> LDS with global_load_lds_dwordx4 (no register
 // staging), issued between the S^T MFMAs of the stage before they are used;
 // s_waitcnt vmcnt plus a workgroup barrier publish each tile. A stage whose
@@ -354,74 +355,37 @@ void attn_bf16_kernel(const AttnParams p) {
       }
     };
 
-    // ---- S^T = K Q^T: operand reads run kPrefetchK MFMAs ahead; the copy of
-    // the next stage is issued in small steps between the MFMAs ----
-    f32x16 sacc[KT];
-    auto qk_product = [&](auto issue) {
-      // K operand of step (t, s): key 32*t + l32, chunk 2*s + h, swizzled
-      // by l32 & (CPR-1); the chunk bits of s enter as an XOR with 32*s.
-      auto read_k = [&](int idx) -> bf16x8 {
-        const int t = idx / DS, s = idx % DS;
-        const char* p = reinterpret_cast<const char*>(sk) + 32 * t * (2 * D) + (k_lane ^ (uint32_t)(32 * s));
-        return bitcast<bf16x8>(*reinterpret_cast<const uint4*>(p));
-      };
-      constexpr int kDmaEvery = (KT * DS) / (2 * LPW) > 0 ? (KT * DS) / (2 * LPW) : 1;
-      bf16x8 ring[kPrefetchK];
-#pragma unroll
-      for (int i = 0; i < kPrefetchK; ++i) ring[i] = read_k(i);
-#pragma unroll
-      for (int idx = 0; idx < KT * DS; ++idx) {
-        const int t = idx / DS, s = idx % DS;
-        const bf16x8 a = ring[idx % kPrefetchK];
-        if (idx + kPrefetchK < KT * DS) ring[idx % kPrefetchK] = read_k(idx + kPrefetchK);
-        sacc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[s], s == 0 ? f32x16{} : sacc[t], 0, 0, 0);
-        if (idx % kDmaEvery == kDmaEvery - 1 && idx / kDmaEvery < 2 * LPW) issue(idx / kDmaEvery);
-        __builtin_amdgcn_sched_barrier(0);   // keep the read-ahead order as written
-      }
-      // (copies that did not fit between the MFMAs, if any)
-#pragma unroll
-      for (int d = (KT * DS) / kDmaEvery; d < 2 * LPW; ++d) issue(d);
-    };
-    if (plain) qk_product(issue_plain);
-    else qk_product(issue_dma);
-
-    // ---- mask keys past N (last block only; a stage wholly past N, the
-    // second half of a short last block, is masked entirely) ----
-    const int valid = n_tok - (c * BLK + half * SUB);
-    if (valid < SUB) {
-      // (opaque bound: keeps the comparisons inside this rarely taken branch)
-      int lv = valid - 4 * h;
-      asm volatile("" : "+v"(lv));
-#pragma unroll
-      for (int t = 0; t < KT; ++t)
-#pragma unroll
-        for (int a = 0; a < 16; ++a) {
-          const int key = 32 * t + 8 * (a >> 2) + (a & 3);
-          if (key >= lv) sacc[t][a] = -INFINITY;
-        }
-    }
-
     // ---- online softmax (fp32, log2 domain, lazy reference maximum) ----
     // Probabilities of stage j are formed against the reference m_run shared
-    // by both key halves of a query, between the PV MFMAs of stage j-1. The
-    // reference moves only when some lane's 32 probabilities of the stage sum
-    // past kStageSumCap or are not finite (the first stage, while m_run is
-    // -inf; masked keys then give NaN): then m_run becomes the maximum so
-    // far, O and l (which hold stages up to j-1, relative to the old
-    // reference) are scaled by alpha, and the stage's probabilities are
-    // formed again. So the row maximum is searched only on those rare stages
-    // and every probability kept is at most 2^13; numerator and denominator
-    // share the reference, so a stale one is exact algebra.
-    // Probabilities go to bf16 in pairs; the row sum adds those same bf16
-    // values (v_dot2 against 1.0), so numerator and denominator of O use
+    // by both key halves of a query. The reference moves only when some
+    // lane's 32 probabilities of the stage sum past kStageSumCap or are not
+    // finite (the first stage, while m_run is -inf; masked keys then give
+    // NaN): then m_run becomes the maximum so far, O and l (which hold stages
+    // up to j-1, relative to the old reference) are scaled by alpha, and the
+    // stage's probabilities are formed again. So the row maximum is searched
+    // only on those rare stages and every probability kept is at most 2^13;
+    // numerator and denominator share the reference, so a stale one is exact
+    // algebra. Probabilities go to bf16 in pairs; the row sum adds those same
+    // bf16 values (v_dot2 against 1.0), so numerator and denominator of O use
     // identical weights.
     float neg_m = -m_run;
     const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
     float psum0 = 0.0f, psum1 = 0.0f;
     float f32sum0 = 0.0f, f32sum1 = 0.0f;   // (LSE only)
+    f32x16 sacc[KT];
     constexpr int NP = KT * 8;          // probability pairs per lane and stage
     constexpr int NPV = KS * DT;        // PV MFMAs per stage
-    static_assert(NP % NPV == 0, "pairs per PV step");
+    constexpr int NQK = KT * DS;        // QK MFMAs per stage
+    // Placement of the exponentials: the MFMA pipe runs best when the VALU
+    // work between its instructions is thin, so kEarlyPairs pairs of key tile
+    // 0 are formed between the last QK MFMAs (those of the later tiles; tile 0
+    // is complete kQkGap MFMAs before the first of them is read) and the rest
+    // between the PV MFMAs. The order of the pairs, hence every sum, is the
+    // same either way.
+    constexpr int kEarlyPairs = 4;
+    constexpr int kQkGap = 2;
+    constexpr int QS = (DS + kQkGap < NQK) ? DS + kQkGap : NQK - 1;   // first QK step hosting pairs
+    static_assert(kEarlyPairs <= 8 && QS >= DS, "early pairs come from key tile 0");
     auto exp_pair = [&](int q) -> uint32_t {
       const int t = q >> 3, a = 2 * (q & 7);
       const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[t][a], scale_log2, neg_m));
@@ -437,9 +401,9 @@ void attn_bf16_kernel(const AttnParams p) {
       pk_cur[2 * t + (a >> 3)][(a & 7) >> 1] = bits;
       return bits;
     };
-    auto exp_pairs = [&](int idx) {     // pairs [idx, idx+1) * NP/NPV
+    auto exp_range = [&](int q0, int q1) {   // pairs [q0, q1)
 #pragma unroll
-      for (int q = idx * (NP / NPV); q < (idx + 1) * (NP / NPV); ++q) {
+      for (int q = q0; q < q1; ++q) {
         const uint32_t bits = exp_pair(q);
         // Anchors: the results are first used after the PV product, and the
         // compiler would otherwise sink this work below its MFMAs.
@@ -448,7 +412,64 @@ void attn_bf16_kernel(const AttnParams p) {
         if constexpr (LSE) asm volatile("" : "+v"(f32sum0), "+v"(f32sum1));
       }
     };
-    // ---- O^T += V_{j-1}^T P_{j-1}^T, with the probabilities of stage j in between ----
+    // Keys past N (last block only; a stage wholly past N, the second half of
+    // a short last block, is masked entirely), per 32-key tile of S^T.
+    const int valid = n_tok - (c * BLK + half * SUB);
+    auto mask_tile = [&](int t) {
+      if (valid < SUB) {
+        // (opaque bound: keeps the comparisons inside this rarely taken branch)
+        int lv = valid - 4 * h;
+        asm volatile("" : "+v"(lv));
+#pragma unroll
+        for (int a = 0; a < 16; ++a) {
+          const int key = 32 * t + 8 * (a >> 2) + (a & 3);
+          if (key >= lv) sacc[t][a] = -INFINITY;
+        }
+      }
+    };
+
+    // ---- S^T = K Q^T: operand reads run kPrefetchK MFMAs ahead; the copy of
+    // the next stage is issued in small steps between the MFMAs, and the
+    // early probability pairs after tile 0 is complete ----
+    auto qk_product = [&](auto issue) {
+      // K operand of step (t, s): key 32*t + l32, chunk 2*s + h, swizzled
+      // by l32 & (CPR-1); the chunk bits of s enter as an XOR with 32*s.
+      auto read_k = [&](int idx) -> bf16x8 {
+        const int t = idx / DS, s = idx % DS;
+        const char* p = reinterpret_cast<const char*>(sk) + 32 * t * (2 * D) + (k_lane ^ (uint32_t)(32 * s));
+        return bitcast<bf16x8>(*reinterpret_cast<const uint4*>(p));
+      };
+      constexpr int kDmaEvery = (KT * DS) / (2 * LPW) > 0 ? (KT * DS) / (2 * LPW) : 1;
+      bf16x8 ring[kPrefetchK];
+#pragma unroll
+      for (int i = 0; i < kPrefetchK; ++i) ring[i] = read_k(i);
+#pragma unroll
+      for (int idx = 0; idx < NQK; ++idx) {
+        const int t = idx / DS, s = idx % DS;
+        const bf16x8 a = ring[idx % kPrefetchK];
+        if (idx + kPrefetchK < NQK) ring[idx % kPrefetchK] = read_k(idx + kPrefetchK);
+        sacc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[s], s == 0 ? f32x16{} : sacc[t], 0, 0, 0);
+        if (idx % kDmaEvery == kDmaEvery - 1 && idx / kDmaEvery < 2 * LPW) issue(idx / kDmaEvery);
+        if (idx >= QS) {
+          if (idx == QS) mask_tile(0);
+          const int i = idx - QS;
+          exp_range(i * kEarlyPairs / (NQK - QS), (i + 1) * kEarlyPairs / (NQK - QS));
+        }
+        __builtin_amdgcn_sched_barrier(0);   // keep the read-ahead order as written
+      }
+      // (copies that did not fit between the MFMAs, if any)
+#pragma unroll
+      for (int d = NQK / kDmaEvery; d < 2 * LPW; ++d) issue(d);
+    };
+    if (plain) qk_product(issue_plain);
+    else qk_product(issue_dma);
+#pragma unroll
+    for (int t = 1; t < KT; ++t) mask_tile(t);
+
+    // ---- O^T += V_{j-1}^T P_{j-1}^T, with the remaining pairs of stage j in between ----
+    auto exp_pairs = [&](int idx) {
+      exp_range(kEarlyPairs + idx * (NP - kEarlyPairs) / NPV, kEarlyPairs + (idx + 1) * (NP - kEarlyPairs) / NPV);
+    };
     pv_product(svp, pk_prev, exp_pairs);
     if (__ballot(!(psum0 + psum1 <= kStageSumCap)) != 0) {
       asm volatile("");   // rare: keep it a branch
