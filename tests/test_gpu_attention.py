@@ -125,8 +125,12 @@ def test_block_sparse_moving_maximum(kind, dtype, N, d, B):
 
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 @pytest.mark.parametrize("d", [64, 128])
+# The broadcast maps grid blocks to (head, frame, row) in runs of 8*R blocks
+# (one frame per XCD) and keeps plain order for a last, partial run: (5, 6, 8)
+# and (7, 3, 9) over two heads give one full run, then a partial one that
+# starts inside the second head.
 @pytest.mark.parametrize("F,R,C,anchors", [(3, 10, 20, [2, 7]), (2, 16, 16, [4, 12]), (2, 5, 30, [0, 1, 2, 3, 4]),
-                                           (4, 9, 7, [4])])
+                                           (4, 9, 7, [4]), (5, 6, 8, [1, 4]), (7, 3, 9, [1])])
 def test_anchor_small(dtype, d, F, R, C, anchors):
     say(f"[anchor] dtype={dtype} d={d} F={F} R={R} C={C} anchors={anchors}")
     H = 2
