@@ -14,7 +14,8 @@
 //   3. add_offsets: every segment but the first adds the previous segment's
 //      global end to its other entries.
 //   4. fill: one wave per row compacts the column indices of nonzero bytes.
-//   5. order: one workgroup per record ranks query blocks by (-count, index).
+//   5. order: query blocks of each record ranked by (-count, index), one
+//      workgroup per group of 64 rows of a record.
 // The interval form (one [lo, hi) pair per maximal run of kept blocks: the
 // contiguous key-block intervals of the same Key Design 4) reuses the scan:
 // run_count counts run openings, run_fill writes each run's two ends (and,
@@ -220,22 +221,75 @@ __global__ __launch_bounds__(kThreads) void fill_kernel(const uint8_t* __restric
   }
 }
 
-__global__ __launch_bounds__(kThreads) void order_kernel(const int64_t* __restrict__ row_ptr, int nb,
-                                                         int32_t* __restrict__ order) {
-  extern __shared__ int32_t cnt[];
-  const int64_t row0 = (int64_t)blockIdx.x * nb;
-  for (int r = threadIdx.x; r < nb; r += kThreads)
-    cnt[r] = (int32_t)(row_ptr[row0 + r + 1] - row_ptr[row0 + r]);
-  __syncthreads();
-  for (int r = threadIdx.x; r < nb; r += kThreads) {
-    const int c = cnt[r];
+// ---- heaviest-first order of the query blocks of each record ----
+//
+// Rows are ranked by (count descending, row ascending): with the key
+// key(x) = count(x) * 4096 + (4095 - x), distinct per row since x < 4096,
+// rank(r) = #{x : key(x) > key(r)} and order[rank] = r. A workgroup holds
+// all keys of one record in LDS, padded to a multiple of four with -1 (below
+// every key), and ranks groups of 64 rows: lane l of wave w ranks row
+// 64*group + l against the w-th quarter of the keys, read four at a time with
+// broadcast reads, and the quarters' partial ranks are added in LDS. With few
+// records (one layer's) each workgroup takes one group, so the ranking spreads
+// over the chip; with many, one workgroup takes all groups of a record.
+__device__ __forceinline__ int order_padded(int nb) { return (nb + 3) & ~3; }
+
+__device__ __forceinline__ int32_t order_key(int count, int x) { return count * 4096 + (4095 - x); }
+
+template <int W>   // waves of the workgroup; wave w scans the w-th W-th of the keys
+__device__ __forceinline__ void rank_groups(const int32_t* key, int nb, int64_t row0, int g0, int g1,
+                                            int32_t* __restrict__ order) {
+  __shared__ int32_t part[64 * W];
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int4* k4 = reinterpret_cast<const int4*>(key);
+  const int n4 = order_padded(nb) / 4;
+  const int per = (n4 + W - 1) / W;
+  const int i0 = wave * per;
+  const int i1 = min(n4, i0 + per);
+  for (int g = g0; g < g1; ++g) {
+    const int r = 64 * g + lane;
+    const int kr = r < nb ? key[r] : 0;   // (lanes past the record rank nothing)
     int rank = 0;
-    for (int x = 0; x < nb; ++x) {
-      const int cx = cnt[x];
-      rank += (cx > c) || (cx == c && x < r);
+#pragma unroll 4
+    for (int i = i0; i < i1; ++i) {
+      const int4 v = k4[i];
+      rank += (v.x > kr) + (v.y > kr) + (v.z > kr) + (v.w > kr);
     }
-    order[row0 + rank] = r;
+    part[threadIdx.x] = rank;
+    __syncthreads();
+    if (wave == 0 && r < nb) {
+      int total = 0;
+#pragma unroll
+      for (int w = 0; w < W; ++w) total += part[64 * w + lane];
+      order[row0 + total] = r;
+    }
+    __syncthreads();   // (part is reused by the next group)
   }
+}
+
+// Workgroup b: record b / per_rec, groups [(b % per_rec) * gpw, ... + gpw).
+struct OrderSlice {
+  int64_t row0;
+  int g0, g1;
+};
+__device__ __forceinline__ OrderSlice order_slice(int nb, int gpw) {
+  const int groups = (nb + 63) / 64;
+  const int per_rec = (groups + gpw - 1) / gpw;
+  const int64_t rec = blockIdx.x / per_rec;
+  const int j = (int)(blockIdx.x - rec * per_rec);
+  return {rec * nb, j * gpw, min(groups, (j + 1) * gpw)};
+}
+
+__global__ __launch_bounds__(kThreads) void order_kernel(const int64_t* __restrict__ row_ptr, int nb, int gpw,
+                                                         int32_t* __restrict__ order) {
+  extern __shared__ int4 order_lds[];
+  int32_t* key = reinterpret_cast<int32_t*>(order_lds);
+  const OrderSlice sl = order_slice(nb, gpw);
+  for (int r = threadIdx.x; r < order_padded(nb); r += kThreads)
+    key[r] = r < nb ? order_key((int)(row_ptr[sl.row0 + r + 1] - row_ptr[sl.row0 + r]), r) : -1;
+  __syncthreads();
+  rank_groups<kWaves>(key, nb, sl.row0, sl.g0, sl.g1, order);
 }
 
 // ---- interval form: one [lo, hi) pair per maximal run of kept key blocks ----
@@ -325,22 +379,21 @@ __global__ __launch_bounds__(kThreads) void run_fill_kernel(const uint8_t* __res
   }
 }
 
-// Same ranking as order_kernel; each row's kept count was left in order[]
-// by run_fill, and is read into LDS before the ranks overwrite it.
-__global__ __launch_bounds__(kThreads) void run_order_kernel(int nb, int32_t* __restrict__ order) {
-  extern __shared__ int32_t cnt[];
-  const int64_t row0 = (int64_t)blockIdx.x * nb;
-  for (int r = threadIdx.x; r < nb; r += kThreads) cnt[r] = order[row0 + r];
+// Same ranking as order_kernel; each row's kept count was left in order[] by
+// run_fill. One workgroup takes all groups of a record, and reads every count
+// into LDS before the ranks overwrite them; it has 16 waves, so that a single
+// layer's few records still keep every SIMD of their CUs busy.
+constexpr int kRunOrderThreads = 1024;
+
+__global__ __launch_bounds__(kRunOrderThreads) void run_order_kernel(int nb, int32_t* __restrict__ order) {
+  extern __shared__ int4 order_lds[];
+  int32_t* key = reinterpret_cast<int32_t*>(order_lds);
+  const int groups = (nb + 63) / 64;
+  const OrderSlice sl = order_slice(nb, groups);
+  for (int r = threadIdx.x; r < order_padded(nb); r += kRunOrderThreads)
+    key[r] = r < nb ? order_key(order[sl.row0 + r], r) : -1;
   __syncthreads();
-  for (int r = threadIdx.x; r < nb; r += kThreads) {
-    const int c = cnt[r];
-    int rank = 0;
-    for (int x = 0; x < nb; ++x) {
-      const int cx = cnt[x];
-      rank += (cx > c) || (cx == c && x < r);
-    }
-    order[row0 + rank] = r;
-  }
+  rank_groups<kRunOrderThreads / 64>(key, nb, sl.row0, sl.g0, sl.g1, order);
 }
 
 // Segmented in-place scan of row_ptr[1 .. rows] (counts -> running sums).
@@ -384,10 +437,25 @@ hipError_t launch_compile_fill(const uint8_t* masks, int64_t rows, int nb, const
   return hipGetLastError();
 }
 
+// Groups of 64 rows per ordering workgroup: one, while the records' groups
+// alone do not fill the chip many times over; else all groups of a record
+// (its keys are then loaded once).
+static int order_groups_per_wg(int64_t records, int nb) {
+  const int groups = (nb + 63) / 64;
+  return records * groups <= 8192 ? 1 : groups;
+}
+
+static unsigned order_grid(int64_t records, int nb, int gpw) {
+  const int groups = (nb + 63) / 64;
+  return (unsigned)(records * ((groups + gpw - 1) / gpw));
+}
+
 hipError_t launch_compile_order(const int64_t* row_ptr, int64_t records, int nb, int32_t* order,
                                 hipStream_t s) {
-  hipLaunchKernelGGL(order_kernel, dim3((unsigned)records), dim3(kThreads), (size_t)nb * sizeof(int32_t), s,
-                     row_ptr, nb, order);
+  const int gpw = order_groups_per_wg(records, nb);
+  const size_t lds = (size_t)((nb + 3) & ~3) * sizeof(int32_t);
+  hipLaunchKernelGGL(order_kernel, dim3(order_grid(records, nb, gpw)), dim3(kThreads), lds, s, row_ptr, nb, gpw,
+                     order);
   return hipGetLastError();
 }
 
@@ -411,8 +479,8 @@ hipError_t launch_compile_runs_fill(const uint8_t* masks, int64_t rows, int nb, 
 }
 
 hipError_t launch_compile_runs_order(int64_t records, int nb, int32_t* order, hipStream_t s) {
-  hipLaunchKernelGGL(run_order_kernel, dim3((unsigned)records), dim3(kThreads), (size_t)nb * sizeof(int32_t), s,
-                     nb, order);
+  const size_t lds = (size_t)((nb + 3) & ~3) * sizeof(int32_t);
+  hipLaunchKernelGGL(run_order_kernel, dim3((unsigned)records), dim3(kRunOrderThreads), lds, s, nb, order);
   return hipGetLastError();
 }
 
