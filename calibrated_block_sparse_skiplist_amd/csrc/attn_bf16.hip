@@ -139,7 +139,8 @@ void attn_bf16_kernel(const AttnParams p) {
   const int h = lane >> 5;               // half of the wave
   const int l32 = lane & 31;
 
-  const Item it = decode_item(p, xcd_item(blockIdx.x, gridDim.x, p.xcd_group));
+  const Item it = decode_item(p, xcd_item_after(blockIdx.x, gridDim.x, p.xcd_group,
+                                                (int64_t)p.n_anchor * p.anchor_tiles, p.xcd_rotate != 0));
   // Scalars used inside the loop, pinned in registers: if the compiler reloads
   // them from the kernel arguments, each scalar load (which returns out of
   // order) forces every following LDS wait to drain completely.

@@ -63,6 +63,24 @@ __device__ __forceinline__ int64_t xcd_item(int64_t b, int64_t total, int G) {
   return run * 8 * (int64_t)G + (s % 8) * G + s / 8;
 }
 
+// The same for a grid whose first `first` items are all of one size: those
+// keep grid order (round-robin gives every XCD the same number of them), and
+// the runs of 8*G blocks are counted from `first`. With `rotate`, run k gives
+// XCD x the G items of chunk (x + k) mod 8 instead of chunk x. Where every run
+// covers whole heads, chunk x would otherwise hold the same slice of every
+// head on the same XCD; slices at the ends of the sequence carry less work,
+// and the XCDs would finish at different times.
+__device__ __forceinline__ int64_t xcd_item_after(int64_t b, int64_t total, int G, int64_t first, bool rotate) {
+  if (b < first || G <= 0) return b;
+  const int64_t t = b - first;
+  const int64_t run = t / (8 * (int64_t)G);
+  if ((run + 1) * 8 * (int64_t)G > total - first) return b;
+  const int64_t s = t - run * 8 * (int64_t)G;   // blocks of XCD b % 8 in this run: s / 8 = 0 .. G-1
+  const int x = (int)(b & 7);
+  const int chunk = rotate ? (int)((x + run) & 7) : x;
+  return first + run * 8 * (int64_t)G + (int64_t)chunk * G + s / 8;
+}
+
 // One 16-byte HBM -> LDS copy (global_load_lds_dwordx4): lane l's chunk lands
 // in slot l of the 64-slot window at `lds` (LDS address = M0 + 16 * lane).
 // The source is a uniform base (SGPR pair) plus this lane's 32-bit offset.

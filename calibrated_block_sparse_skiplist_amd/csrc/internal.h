@@ -18,10 +18,12 @@ namespace calibatt {
 //     query block j % nb (or order[rec*nb + j % nb] when use_order is set and
 //     order is given; the entry points leave use_order at 0).
 // Grid blocks map to items
-// XCD-aware: workgroups are dispatched round-robin over the 8 XCDs, so within
-// each run of 8 * xcd_group grid blocks XCD x receives xcd_group consecutive
-// items; neighbouring query blocks share most of their key blocks, which then
-// stay in that XCD's L2.
+// XCD-aware: workgroups are dispatched round-robin over the 8 XCDs, so each
+// XCD's share of the grid is fixed in advance. Anchor items (all of one size)
+// keep grid order; block-sparse items go in runs of 8 * xcd_group grid blocks,
+// XCD x receiving xcd_group consecutive items per run (neighbouring query
+// blocks share most of their key blocks, which then stay in that XCD's L2),
+// and with xcd_rotate the chunk each XCD takes turns by one per run.
 struct AttnParams {
   const void* q;
   const void* k;
@@ -44,6 +46,7 @@ struct AttnParams {
   int32_t n_sparse;
   int32_t use_order;        // 1: visit query blocks heaviest-first; 0: in block order
   int32_t xcd_group;        // consecutive items given to one XCD (0: plain grid order)
+  int32_t xcd_rotate;       // 1: the chunk of each XCD turns per run (runs that cover whole heads)
   // anchor items
   int32_t n_anchor;
   int32_t anchor_tiles;

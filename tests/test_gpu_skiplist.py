@@ -29,6 +29,10 @@ def _compile_and_compare(masks: np.ndarray, N: int, B: int, label: str):
     ((1, 1, 1, 1), 1.0, 0), ((1, 1, 1, 1), 0.0, 1), ((1, 1, 2, 3), 0.5, 2), ((2, 3, 2, 7), 0.4, 3),
     ((1, 1, 3, 64), 0.3, 4), ((1, 1, 2, 65), 0.7, 5), ((1, 2, 5, 131), 0.2, 6), ((3, 1, 2, 300), 0.05, 7),
     ((1, 1, 1, 1030), 0.5, 8),
+    # sparse rows: counts 0..~15, so most ranks are decided by the row index
+    ((1, 1, 2, 591), 0.01, 10),
+    # nb = CALIBATT_MAX_NB: 64 groups of 64 rows in the ranking
+    ((1, 1, 1, 4096), 0.002, 11),
 ])
 def test_random_masks(shape, p, seed):
     rng = np.random.default_rng(seed)
