@@ -35,7 +35,17 @@ sys.path.insert(0, ROOT)
 PEAK_BF16_TFLOPS = 2516.6     # MI355X dense bf16 MFMA: 256 CU x 2.4 GHz x 4096 FLOP/clk
 PEAK_HBM_GBS = 8000.0
 ATTN_KERNEL = "attn_bf16_kernel"
-ATTN_SOURCE = os.path.join(ROOT, "calibrated_block_sparse_skiplist_amd", "csrc", "attn_bf16.hip")
+# Sources the bf16 attention kernel is compiled from (its own file and the headers it includes).
+ATTN_SOURCES = [os.path.join(ROOT, "calibrated_block_sparse_skiplist_amd", "csrc", f)
+                for f in ("attn_bf16.hip", "gfx950_device.h", "internal.h")]
+
+
+def attn_source_sha() -> str:
+    """sha256 over the attention kernel's sources, in order: the key that ties a counter profile to a build."""
+    h = hashlib.sha256()
+    for path in ATTN_SOURCES:
+        h.update(open(path, "rb").read())
+    return h.hexdigest()
 
 
 def parse_args():
@@ -629,8 +639,7 @@ def main():
 
     flops = work["flops"]
     achieved = flops / (attn_ms * 1e-3) / 1e12
-    sha = hashlib.sha256(open(ATTN_SOURCE, "rb").read()).hexdigest()
-    traffic = pmc_traffic(sha)
+    traffic = pmc_traffic(attn_source_sha())
     value = flops / (ms_per_step * 1e-3) / 1e12
     res = {
         "metric": "ms per attention layer-call + retained-block TFLOP/s (% of bf16 MFMA peak)",
