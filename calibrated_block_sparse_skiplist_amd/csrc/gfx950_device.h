@@ -63,15 +63,20 @@ __device__ __forceinline__ int64_t xcd_item(int64_t b, int64_t total, int G) {
   return run * 8 * (int64_t)G + (s % 8) * G + s / 8;
 }
 
-// The same for a grid whose first `first` items are all of one size: those
-// keep grid order (round-robin gives every XCD the same number of them), and
-// the runs of 8*G blocks are counted from `first`. With `rotate`, run k gives
-// XCD x the G items of chunk (x + k) mod 8 instead of chunk x. Where every run
-// covers whole heads, chunk x would otherwise hold the same slice of every
-// head on the same XCD; slices at the ends of the sequence carry less work,
-// and the XCDs would finish at different times.
+// The same for a grid whose first `first` items are all of one size: XCD x
+// takes one chunk of first/8 consecutive ones (equal counts, and neighbouring
+// items on one L2), the few left over keep grid order, and the runs of 8*G
+// blocks are counted from `first`. With `rotate`, run k gives XCD x the G
+// items of chunk (x + k) mod 8 instead of chunk x. Where every run covers
+// whole heads, chunk x would otherwise hold the same slice of every head on
+// the same XCD; slices at the ends of the sequence carry less work, and the
+// XCDs would finish at different times.
 __device__ __forceinline__ int64_t xcd_item_after(int64_t b, int64_t total, int G, int64_t first, bool rotate) {
-  if (b < first || G <= 0) return b;
+  if (b < first) {
+    const int64_t per_xcd = first / 8;
+    return b < 8 * per_xcd ? (b & 7) * per_xcd + b / 8 : b;
+  }
+  if (G <= 0) return b;
   const int64_t t = b - first;
   const int64_t run = t / (8 * (int64_t)G);
   if ((run + 1) * 8 * (int64_t)G > total - first) return b;

@@ -20,7 +20,8 @@ namespace calibatt {
 // Grid blocks map to items
 // XCD-aware: workgroups are dispatched round-robin over the 8 XCDs, so each
 // XCD's share of the grid is fixed in advance. Anchor items (all of one size)
-// keep grid order; block-sparse items go in runs of 8 * xcd_group grid blocks,
+// go one chunk of n/8 consecutive items per XCD; block-sparse items go in runs
+// of 8 * xcd_group grid blocks,
 // XCD x receiving xcd_group consecutive items per run (neighbouring query
 // blocks share most of their key blocks, which then stay in that XCD's L2),
 // and with xcd_rotate the chunk each XCD takes turns by one per run.
