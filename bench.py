@@ -461,7 +461,8 @@ def main():
     args = parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
-              "(the layer shards by head with no communication; see the design notes)", file=sys.stderr)
+              "(a layer shards by head with no communication: each GPU would run this single-GPU workload on its share "
+              "of the heads)", file=sys.stderr)
         sys.exit(2)
     import torch
     if args.dictionary_sweep:
