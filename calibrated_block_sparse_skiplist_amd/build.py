@@ -27,6 +27,10 @@ FLAGS = [
     "-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
     # Packed fp32 VALU forms stay disabled: the scalar fp32 forms are used throughout.
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # MFMA results in VGPRs, not AGPRs: the score accumulators are read by VALU
+    # work (exponentials), and an AGPR operand costs a v_accvgpr_read first
+    # (the block-energy kernel: 32 per stage and wave, and one wave less per SIMD).
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
     "-Wno-unused-result", "-Wno-unused-command-line-argument",
     "-I", INCLUDE, "-I", CSRC,
 ]
