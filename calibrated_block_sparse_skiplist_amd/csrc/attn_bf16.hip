@@ -11,7 +11,9 @@
 // CU (register budget capped at 256 per lane; 72 KB of LDS each: K and V
 // double buffers plus the item's staged key-block list), so each SIMD runs
 // two waves that cover each other's waits. Keys are visited in
-// stages of 64 (two per 128-key block). In stage j each wave
+// stages of 64 (two per 128-key block; 64-token blocks take stages of 32,
+// which halve the K/V buffers so that four workgroups share a CU and each
+// SIMD still runs two waves). In stage j each wave
 //   1. computes S^T_j = K_j Q^T with v_mfma_f32_32x32x16_bf16 (A = K from LDS,
 //      B = Q^T held in registers): every lane owns one query column and half
 //      of the stage's keys;
@@ -112,7 +114,7 @@ template <int D, int BLK, bool LSE>
 __global__ __launch_bounds__(BLK * 2) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void attn_bf16_kernel(const AttnParams p) {
   constexpr int NW = BLK / 32;           // waves per workgroup (32 queries each)
-  constexpr int SUB = 64;                // keys per pipeline stage
+  constexpr int SUB = BLK >= 128 ? 64 : 32;   // keys per pipeline stage (32 for 64-token blocks: half the LDS)
   constexpr int SPB = BLK / SUB;         // stages per key block
   constexpr int CPR = D / 8;             // 16-byte chunks per K/V row
   constexpr int KT = SUB / 32;           // 32-key tiles of S^T per stage
@@ -383,10 +385,10 @@ void attn_bf16_kernel(const AttnParams p) {
     // is complete kQkGap MFMAs before the first of them is read) and the rest
     // between the PV MFMAs. The order of the pairs, hence every sum, is the
     // same either way.
-    constexpr int kEarlyPairs = 4;
+    constexpr int kEarlyPairs = KT > 1 ? 4 : 0;   // (a single key tile has no later QK MFMAs to host them)
     constexpr int kQkGap = 2;
-    constexpr int QS = (DS + kQkGap < NQK) ? DS + kQkGap : NQK - 1;   // first QK step hosting pairs
-    static_assert(kEarlyPairs <= 8 && QS >= DS, "early pairs come from key tile 0");
+    constexpr int QS = KT == 1 ? NQK : (DS + kQkGap < NQK) ? DS + kQkGap : NQK - 1;   // first QK step hosting pairs
+    static_assert(kEarlyPairs <= 8 && (kEarlyPairs == 0 || QS >= DS), "early pairs come from key tile 0");
     auto exp_pair = [&](int q) -> uint32_t {
       const int t = q >> 3, a = 2 * (q & 7);
       const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[t][a], scale_log2, neg_m));
@@ -451,10 +453,12 @@ void attn_bf16_kernel(const AttnParams p) {
         if (idx + kPrefetchK < NQK) ring[idx % kPrefetchK] = read_k(idx + kPrefetchK);
         sacc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[s], s == 0 ? f32x16{} : sacc[t], 0, 0, 0);
         if (idx % kDmaEvery == kDmaEvery - 1 && idx / kDmaEvery < 2 * LPW) issue(idx / kDmaEvery);
-        if (idx >= QS) {
-          if (idx == QS) mask_tile(0);
-          const int i = idx - QS;
-          exp_range(i * kEarlyPairs / (NQK - QS), (i + 1) * kEarlyPairs / (NQK - QS));
+        if constexpr (kEarlyPairs > 0) {
+          if (idx >= QS) {
+            if (idx == QS) mask_tile(0);
+            const int i = idx - QS;
+            exp_range(i * kEarlyPairs / (NQK - QS), (i + 1) * kEarlyPairs / (NQK - QS));
+          }
         }
         __builtin_amdgcn_sched_barrier(0);   // keep the read-ahead order as written
       }
@@ -465,7 +469,7 @@ void attn_bf16_kernel(const AttnParams p) {
     if (plain) qk_product(issue_plain);
     else qk_product(issue_dma);
 #pragma unroll
-    for (int t = 1; t < KT; ++t) mask_tile(t);
+    for (int t = kEarlyPairs > 0 ? 1 : 0; t < KT; ++t) mask_tile(t);
 
     // ---- O^T += V_{j-1}^T P_{j-1}^T, with the remaining pairs of stage j in between ----
     auto exp_pairs = [&](int idx) {
