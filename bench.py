@@ -58,7 +58,8 @@ def parse_args():
     ap.add_argument("--config", default="wan720",
                     choices=["tiny", "wan480_sparse", "wan480_dual", "wan720"])
     ap.add_argument("--dense-reps", type=int, default=3, help="launches of the dense comparator")
-    ap.add_argument("--cpu-seconds", type=float, default=15.0, help="budget of the CPU oracle sample")
+    ap.add_argument("--cpu-seconds", type=float, default=20.0,
+                    help="time budget of each CPU oracle worker (the baseline's bounded sample)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-dense", action="store_true")
     ap.add_argument("--copy-calib", action="store_true",
@@ -76,6 +77,8 @@ def parse_args():
                          "40 heads) resident on the GPU: compile both list forms, account memory, and stream "
                          "layer calls through sampled timesteps (one JSON line)")
     ap.add_argument("--run-steps", default="0,25,49", help="timesteps whose 40 layer calls are timed")
+    ap.add_argument("--no-extra-configs", action="store_true",
+                    help="skip the 480p layers and the sweep summary in the default run")
     return ap.parse_args()
 
 
@@ -121,56 +124,104 @@ def layer_work(wl):
 
 
 # ---------------------------------------------------------------------------
-# CPU oracle baseline on a bounded sample
+# CPU oracle baseline: a process pool over a stated subset of heads
 # ---------------------------------------------------------------------------
-def cpu_baseline(wl, budget_s: float):
+CPU_POOL_CAP = 16     # host cores that go with one GPU on the measurement boxes
+
+
+def _oracle_worker(job):
+    """One pool worker: evaluates oracle units (a query block of a block-sparse head, or one frame of
+    an anchor head) from its share until its time budget is spent, with BLAS on one thread.
+    Returns (FLOP done, seconds busy, units done)."""
+    tmp, meta, units, budget = job
+    from threadpoolctl import threadpool_limits
+    import oracle
+    q = np.load(os.path.join(tmp, "q.npy"), mmap_mode="r")
+    k = np.load(os.path.join(tmp, "k.npy"), mmap_mode="r")
+    v = np.load(os.path.join(tmp, "v.npy"), mmap_mode="r")
+    rp = np.load(os.path.join(tmp, "rp.npy"))
+    ci = np.load(os.path.join(tmp, "ci.npy"))
+    N, d, B = meta["N"], meta["d"], meta["B"]
+    sizes = block_sizes(N, B)
+    flop, done = 0.0, 0
+    with threadpool_limits(1):
+        t0 = time.perf_counter()
+        for kind, slot, idx in units:
+            if time.perf_counter() - t0 >= budget:
+                break
+            if kind == "anchor":
+                oracle.anchor_head(q[slot], k[slot], v[slot], meta["F"], meta["R"], meta["C"], meta["anchors"],
+                                   meta["scale"], frames=[idx])
+                flop += 4.0 * d * len(meta["anchors"]) * meta["C"] * N
+            else:
+                oracle.block_sparse_head(q[slot], k[slot], v[slot], rp, ci, slot, B, meta["scale"], blocks=[idx])
+                row = slot * len(sizes) + idx
+                flop += 4.0 * d * sizes[idx] * float(sizes[ci[rp[row]:rp[row + 1]]].sum())
+            done += 1
+        busy = time.perf_counter() - t0
+    return flop, busy, done
+
+
+def cpu_baseline(wl, budget_s: float, flops_layer: float):
+    """The fp64 oracle on the host cores: a process pool (one worker per core, up to the cores that go
+    with one GPU; BLAS on one thread per worker) over a subset of the layer's heads, 4 block-sparse heads
+    and 1 anchor head. Each worker takes a shuffled share of the subset's units (query blocks of the
+    sparse heads, frames of the anchor head) and runs them until `budget_s` of its own time is spent.
+    The rate is the sum of the workers' FLOP/s (they run concurrently); the full layer's oracle time is
+    extrapolated from it by algorithmic FLOP."""
+    import multiprocessing as mp
+    import shutil
+    import tempfile
     import oracle
     import workloads
-    try:
-        from threadpoolctl import threadpool_info
-        cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-    except Exception:
-        cores = 1
     cfg = wl.cfg
-    rp, ci, _ = oracle.compile_skiplist(wl.masks)
+    cores_visible = len(os.sched_getaffinity(0))
+    workers = max(1, min(cores_visible, CPU_POOL_CAP))
     flags = wl.rep_flags[0, 0]
     sparse = [h for h in range(cfg.H) if not flags[h]]
     rep = [h for h in range(cfg.H) if flags[h]]
     rng = np.random.default_rng(123)
-    flops = 0.0
-    t_used = 0.0
-    n_blocks = 0
-    n_frames = 0
-    sizes = block_sizes(cfg.N, cfg.B)
-    as_f = workloads.bf16_to_f32 if cfg.dtype == "bf16" else (lambda x: x)
-    # one anchor frame first (if any), then random sparse query blocks until the budget is spent
-    if rep:
-        h = rep[0]
-        qh, kh, vh = as_f(wl.q[h]), as_f(wl.k[h]), as_f(wl.v[h])
-        t0 = time.perf_counter()
-        oracle.anchor_head(qh, kh, vh, cfg.F, cfg.R, cfg.C, wl.anchors, wl.scale, frames=[0])
-        t_used += time.perf_counter() - t0
-        flops += 4.0 * cfg.d * len(wl.anchors) * cfg.C * cfg.N
-        n_frames += 1
-    cache = {}
-    while t_used < budget_s and sparse:
-        h = int(rng.choice(sparse))
-        r = int(rng.integers(cfg.nb))
-        if h not in cache:
-            cache = {h: (as_f(wl.q[h]), as_f(wl.k[h]), as_f(wl.v[h]))}
-        qh, kh, vh = cache[h]
-        t0 = time.perf_counter()
-        oracle.block_sparse_head(qh, kh, vh, rp, ci, h, cfg.B, wl.scale, blocks=[r])
-        t_used += time.perf_counter() - t0
-        row = h * cfg.nb + r
-        cols = ci[rp[row]:rp[row + 1]]
-        flops += 4.0 * cfg.d * sizes[r] * float(sizes[cols].sum())
-        n_blocks += 1
-    value = flops / t_used / 1e12 if t_used > 0 else None
-    return {"value": value, "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
-            "sample": f"fp64 numpy oracle on {n_blocks} random block-sparse query blocks and {n_frames} anchor "
-                      f"frame(s) of the same layer: {flops / 1e12:.4f} TFLOP in {t_used:.1f} s",
-            "seconds": t_used, "tflop": flops / 1e12}
+    sub_sparse = sorted(int(h) for h in rng.choice(sparse, size=min(4, len(sparse)), replace=False))
+    sub_rep = [int(rep[0])] if rep else []
+    heads = sub_sparse + sub_rep
+    as_f = workloads.bf16_to_f32 if cfg.dtype == "bf16" else (lambda x: np.asarray(x, np.float32))
+    tmp = tempfile.mkdtemp(prefix="calibatt_oracle_")
+    try:
+        # the subset's exact input values in fp64 (the oracle's precision), shared by the workers
+        for name, arr in (("q", wl.q), ("k", wl.k), ("v", wl.v)):
+            np.save(os.path.join(tmp, f"{name}.npy"), np.stack([as_f(arr[h]).astype(np.float64) for h in heads]))
+        # lists of the subset's sparse heads (records renumbered to the subset's slots)
+        sub_masks = wl.masks[:, :, sub_sparse] if sub_sparse else wl.masks[:, :, :0]
+        rp, ci, _ = oracle.compile_skiplist(sub_masks)
+        np.save(os.path.join(tmp, "rp.npy"), rp)
+        np.save(os.path.join(tmp, "ci.npy"), ci)
+        units = [("sparse", i, r) for i in range(len(sub_sparse)) for r in range(cfg.nb)]
+        units += [("anchor", len(sub_sparse) + i, f) for i in range(len(sub_rep)) for f in range(cfg.F)]
+        order = rng.permutation(len(units))
+        units = [units[i] for i in order]
+        meta = {"N": cfg.N, "d": cfg.d, "B": cfg.B, "F": cfg.F, "R": cfg.R, "C": cfg.C,
+                "anchors": [int(a) for a in wl.anchors], "scale": wl.scale}
+        jobs = [(tmp, meta, units[w::workers], budget_s) for w in range(workers)]
+        with mp.get_context("spawn").Pool(workers) as pool:
+            res = pool.map(_oracle_worker, jobs)
+    finally:
+        shutil.rmtree(tmp, ignore_errors=True)
+    flop = sum(r[0] for r in res)
+    rate = sum(r[0] / r[1] for r in res if r[1] > 0)
+    done = sum(r[2] for r in res)
+    n_sp = sum(1 for u in units if u[0] == "sparse")
+    value = rate / 1e12 if rate > 0 else None
+    return {"value": value, "unit": "TFLOP/s", "cores": workers, "kind": "oracle",
+            "sample": f"fp64 numpy oracle, process pool of {workers} workers (BLAS 1 thread each) over heads "
+                      f"{sub_sparse} (block-sparse) and {sub_rep} (anchor) of the same layer: {done} of "
+                      f"{len(units)} units ({n_sp} query blocks, {len(units) - n_sp} anchor frames) in "
+                      f"{budget_s:.0f} s per worker, {flop / 1e12:.3f} TFLOP; the full layer extrapolated by "
+                      f"algorithmic FLOP",
+            "cores_visible": cores_visible, "blas_threads_per_worker": 1,
+            "subset_heads": {"block_sparse": sub_sparse, "anchor": sub_rep},
+            "extrapolated": True,
+            "layer_seconds_extrapolated": round(flops_layer / rate, 1) if rate > 0 else None,
+            "tflop_done": round(flop / 1e12, 4)}
 
 
 def pmc_traffic(kernel_sha: str):
@@ -457,6 +508,115 @@ def dictionary_run(args):
         "layer_calls": per_step}), flush=True)
 
 
+def measure_layer_config(key: str, reps: int = 10, dense_reps: int = 2):
+    """A further layer configuration, timed the way the headline is (layer-call = calibatt_layer_dispatch
+    with O only; the attention kernel alone via HIP events on its stream; the same kernel dense over all
+    heads). Returns a small dict for the bench line."""
+    import torch
+    import workloads
+    import calibrated_block_sparse_skiplist_amd as cal
+    wl = workloads.make_workload(key)
+    cfg = wl.cfg
+    work = layer_work(wl)
+    dev = torch.device("cuda")
+    q, k, v = (torch.from_numpy(x.view(np.int16)).view(torch.bfloat16).to(dev) for x in (wl.q, wl.k, wl.v))
+    o = torch.empty_like(q)
+    sl = cal.compile_skiplist(torch.from_numpy(wl.masks).to(dev), cfg.N, cfg.B)
+    stream = torch.cuda.current_stream()
+
+    def call(ev=None):
+        if ev is not None:
+            cal.calibatt_set_kernel_events(ev[0].cuda_event, ev[1].cuda_event)
+        cal.calibatt_layer_dispatch(q, k, v, o, None, sl, 0, 0, wl.rep_flags, cfg.F, cfg.R, cfg.C, wl.anchors,
+                                    scale=wl.scale, stream=stream)
+    for _ in range(2):
+        call()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+    for a, b in evs:
+        a.record(stream)
+        b.record(stream)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for ev in evs:
+        call(ev)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    layer_ms = e0.elapsed_time(e1) / reps
+    kern_ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
+    ones = torch.ones((1, 1, cfg.H, cfg.nb, cfg.nb), dtype=torch.uint8, device=dev)
+    sld = cal.compile_skiplist(ones, cfg.N, cfg.B)
+    cal.calibatt_block_sparse_attn(q, k, v, o, None, sld, 0, 0, scale=wl.scale, stream=stream)
+    e0.record(stream)
+    for _ in range(dense_reps):
+        cal.calibatt_block_sparse_attn(q, k, v, o, None, sld, 0, 0, scale=wl.scale, stream=stream)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    dense_ms = e0.elapsed_time(e1) / dense_reps
+    tf = work["flops"] / (layer_ms * 1e-3) / 1e12
+    return {"workload": f"{cfg.key}: {cfg.title}", "sparse_heads": len(work["sparse_heads"]),
+            "repetitive_heads": len(work["rep_heads"]),
+            "token_sparsity_sparse_heads": round(work["token_sparsity_sparse_heads"], 4),
+            "retained_tflop": round(work["flops"] / 1e12, 3), "layer_call_ms": round(layer_ms, 3),
+            "attn_kernel_ms": round(kern_ms, 3), "tflops": round(tf, 1),
+            "pct_of_bf16_peak": round(100.0 * tf / PEAK_BF16_TFLOPS, 2),
+            "kernel_tflops": round(work["flops"] / (kern_ms * 1e-3) / 1e12, 1),
+            "dense_same_kernel_ms": round(dense_ms, 3), "speedup_vs_dense": round(dense_ms / layer_ms, 3)}
+
+
+def sweep_summary(layers: int = 2):
+    """The 480p dictionary sweep (sparsity 0/50/68/85 % x repetitive fraction 0/10/25 %), cut to its
+    first `layers` layers (the same masks and flags as the first layers of the 40-layer dictionary):
+    per point the compile of those layers' masks and the mean layer-call."""
+    import torch
+    import workloads
+    import calibrated_block_sparse_skiplist_amd as cal
+    base = workloads.get_config("wan480_dual")
+    q, k, v = workloads.make_qkv(base)
+    dev = torch.device("cuda")
+    qd, kd, vd = (torch.from_numpy(x.view(np.int16)).view(torch.bfloat16).to(dev) for x in (q, k, v))
+    del q, k, v
+    o = torch.empty_like(qd)
+    anchors = workloads.equally_spaced_anchor_rows(base.R, base.n_anchor)
+    scale = float(np.float32(1.0 / np.sqrt(base.d)))
+    stream = torch.cuda.current_stream()
+    points = []
+    for sp in (0.0, 0.5, 0.68, 0.85):
+        for rf in (0.0, 0.10, 0.25):
+            cfg, masks, flags = workloads.make_dictionary_workload(sp, rf, L=layers)
+            dm = torch.from_numpy(masks).to(dev)
+            sl = cal.compile_skiplist(dm, cfg.N, cfg.B)
+            t0 = time.perf_counter()
+            cal.calibatt_compile_skiplist(dm, 1, cfg.L, cfg.H, cfg.N, cfg.B, sl.row_ptr, sl.col_idx,
+                                          sl.col_idx.numel(), sl.order, stream)
+            compile_ms = (time.perf_counter() - t0) * 1e3
+            ms, fl = [], []
+            for l in range(cfg.L):
+                cal.calibatt_layer_dispatch(qd, kd, vd, o, None, sl, 0, l, flags, cfg.F, cfg.R, cfg.C, anchors,
+                                            scale=scale, stream=stream)
+                a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                a.record(stream)
+                cal.calibatt_layer_dispatch(qd, kd, vd, o, None, sl, 0, l, flags, cfg.F, cfg.R, cfg.C, anchors,
+                                            scale=scale, stream=stream)
+                b.record(stream)
+                torch.cuda.synchronize()
+                ms.append(a.elapsed_time(b))
+                f = sum(anchor_head_flops(cfg.F, len(anchors), cfg.C, cfg.N, cfg.d) if flags[0, l, h]
+                        else sparse_head_flops(masks[0, l, h], cfg.N, cfg.B, cfg.d) for h in range(cfg.H))
+                fl.append(f)
+            lm = float(np.mean(ms))
+            points.append({"sparsity": sp, "repetitive_fraction": rf,
+                           "block_sparsity": round(1.0 - float(masks.astype(np.float64).mean()), 4),
+                           "compile_ms": round(compile_ms, 3), "layer_call_ms": round(lm, 3),
+                           "tflops": round(float(np.mean(fl)) / (lm * 1e-3) / 1e12, 1)})
+            del dm, sl
+    dense = {p["repetitive_fraction"]: p["layer_call_ms"] for p in points if p["sparsity"] == 0.0}
+    for p in points:
+        p["speedup_vs_dense"] = round(dense[0.0] / p["layer_call_ms"], 3)
+    return {"workload": f"480p dictionary, 40 heads, first {layers} layers per point "
+                        "(speedups against the 0 %-sparsity, 0 %-repetitive point)", "points": points}
+
+
 def main():
     args = parse_args()
     if args.gpus != 1:
@@ -636,7 +796,15 @@ def main():
 
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(wl, args.cpu_seconds)
+        cpu = cpu_baseline(wl, args.cpu_seconds, work["flops"])
+
+    # the other layer configurations and the sweep, measured in the same run (after the headline)
+    extra = None
+    if not args.no_extra_configs and args.config == "wan720":
+        del q, k, v, o, lse, masks, sl
+        torch.cuda.empty_cache()
+        extra = {"configs": [measure_layer_config(key) for key in ("wan480_sparse", "wan480_dual")],
+                 "sweep_480p": sweep_summary()}
 
     flops = work["flops"]
     achieved = flops / (attn_ms * 1e-3) / 1e12
@@ -680,6 +848,7 @@ def main():
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
                      "traffic": traffic, "flop_per_launch": flops, "launch_ms": round(attn_ms, 3)},
         "cpu_baseline": cpu,
+        "other_workloads": extra,
     }
     print(json.dumps(res), flush=True)
 

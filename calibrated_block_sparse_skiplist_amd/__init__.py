@@ -11,6 +11,8 @@ The names follow the C ABI in include/calibatt.h:
   calibration: block energies of a prompt, its top-tau selection, cross-prompt keep frequency
 * ``calibatt_spatial_similarity`` / ``calibatt_repetition_flags`` -- offline calibration: spatial-row
   similarity to the nearest anchor row, and the per-head repetition flags
+* ``calibatt_validate_skiplist`` / ``calibatt_validate_intervals`` / ``calibatt_set_checked_mode`` --
+  checked mode: host-side validation of a list view before it reaches the kernels
 
 All computation happens in the library's HIP kernels; this package only
 marshals arguments. Importing it fails if the library has not been built.
@@ -21,6 +23,7 @@ from ._lib import (BF16, F32, CalibattError, IntervalList, IntervalListView, Ski
                    calibatt_compile_intervals, calibatt_compile_skiplist, calibatt_layer_dispatch,
                    calibatt_layer_dispatch_iv, calibatt_repetition_flags, calibatt_set_kernel_events,
                    calibatt_spatial_similarity, calibatt_version,
+                   calibatt_validate_skiplist, calibatt_validate_intervals, calibatt_set_checked_mode,
                    compile_intervals, compile_skiplist, energy_work_bytes, last_error)
 
 __all__ = ["BF16", "F32", "CalibattError", "IntervalList", "IntervalListView", "SkipList", "SkipListView",
@@ -29,4 +32,5 @@ __all__ = ["BF16", "F32", "CalibattError", "IntervalList", "IntervalListView", "
            "calibatt_compile_intervals", "calibatt_compile_skiplist", "calibatt_layer_dispatch",
            "calibatt_layer_dispatch_iv", "calibatt_repetition_flags", "calibatt_set_kernel_events",
            "calibatt_spatial_similarity", "calibatt_version",
+           "calibatt_validate_skiplist", "calibatt_validate_intervals", "calibatt_set_checked_mode",
            "compile_intervals", "compile_skiplist", "energy_work_bytes", "last_error"]

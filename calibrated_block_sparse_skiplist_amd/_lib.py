@@ -14,7 +14,9 @@ from dataclasses import dataclass
 import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libcalibatt.so")
+# CALIBATT_LIB selects another build of the same library (the host-sanitized
+# one, for CPU runs of the host logic); by default the in-tree build is loaded.
+LIB_PATH = os.environ.get("CALIBATT_LIB") or os.path.join(_HERE, "libcalibatt.so")
 
 OK, ERR_INVALID_ARG, ERR_CAPACITY, ERR_HIP, ERR_UNSUPPORTED = 0, 1, 2, 3, 4
 BF16, F32 = 0, 1
@@ -26,6 +28,7 @@ EXPORTED = (
     "calibatt_layer_dispatch_iv", "calibatt_block_energy", "calibatt_select_blocks", "calibatt_keep_frequency",
     "calibatt_spatial_similarity", "calibatt_repetition_flags",
     "calibatt_last_error", "calibatt_set_kernel_events", "calibatt_version",
+    "calibatt_validate_skiplist", "calibatt_validate_intervals", "calibatt_set_checked_mode",
 )
 
 
@@ -98,6 +101,12 @@ def _load():
     lib.calibatt_set_kernel_events.restype = None
     lib.calibatt_version.argtypes = []
     lib.calibatt_version.restype = i32
+    lib.calibatt_validate_skiplist.argtypes = [ctypes.POINTER(SkipListView), i32, i32, i32, vp]
+    lib.calibatt_validate_skiplist.restype = i32
+    lib.calibatt_validate_intervals.argtypes = [ctypes.POINTER(IntervalListView), i32, i32, i32, vp]
+    lib.calibatt_validate_intervals.restype = i32
+    lib.calibatt_set_checked_mode.argtypes = [i32]
+    lib.calibatt_set_checked_mode.restype = None
     return lib
 
 
@@ -367,3 +376,21 @@ def calibatt_set_kernel_events(begin, end) -> None:
 
 def calibatt_version() -> int:
     return lib.calibatt_version()
+
+
+def calibatt_validate_skiplist(sl: SkipList, t: int = -1, l: int = -1, stream=None) -> None:
+    """Checked mode: validate a SkipList (device tensors) for record (t, l), or all of it (t = l = -1).
+    Raises CalibattError on a malformed view."""
+    view = sl.view()
+    _check(lib.calibatt_validate_skiplist(ctypes.byref(view), t, l, 0, _stream(stream)))
+
+
+def calibatt_validate_intervals(il: IntervalList, t: int = -1, l: int = -1, stream=None) -> None:
+    """Checked mode for an IntervalList (device tensors)."""
+    view = il.view()
+    _check(lib.calibatt_validate_intervals(ctypes.byref(view), t, l, 0, _stream(stream)))
+
+
+def calibatt_set_checked_mode(enabled: bool) -> None:
+    """When enabled (this thread), the attention calls validate their record's lists before launching."""
+    lib.calibatt_set_checked_mode(1 if enabled else 0)

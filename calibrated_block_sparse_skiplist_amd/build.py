@@ -36,12 +36,22 @@ FLAGS = [
 ]
 
 
+# Host-side sanitizer build (address + undefined behaviour) of the same sources,
+# for CPU runs of the host logic (argument checks, list validation). Every
+# sanitizer flag applies to the host compilation only (-Xarch_host): the device
+# code is the ordinary gfx950 code.
+SANITIZE_FLAGS = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+                  "-Xarch_host", "-fno-sanitize-recover=undefined", "-Xarch_host", "-fno-omit-frame-pointer",
+                  "-Xarch_host", "-shared-libasan"]
+SANITIZED_LIB = os.path.join(BUILD_DIR, "sanitized", "libcalibatt.so")
+
+
 def sources() -> list[str]:
     return sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith(".hip"))
 
 
-def _compile(src: str, extra: list[str]) -> str:
-    obj = os.path.join(BUILD_DIR, os.path.basename(src).replace(".hip", ".o"))
+def _compile(src: str, extra: list[str], out_dir: str = BUILD_DIR) -> str:
+    obj = os.path.join(out_dir, os.path.basename(src).replace(".hip", ".o"))
     cmd = [HIPCC, *FLAGS, *extra, "-c", src, "-o", obj]
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
@@ -67,6 +77,33 @@ def build(verbose: bool = False, extra_flags: list[str] | None = None) -> str:
     if verbose:
         print(f"built {LIB_PATH} from {len(srcs)} sources", file=sys.stderr)
     return LIB_PATH
+
+
+def build_sanitized(verbose: bool = False) -> str:
+    """The host-sanitized variant of libcalibatt.so (outside the package: never loaded by default).
+    Load it with the clang ASan runtime preloaded and CALIBATT_LIB set to the returned path."""
+    out_dir = os.path.dirname(SANITIZED_LIB)
+    os.makedirs(out_dir, exist_ok=True)
+    srcs = sources()
+    with concurrent.futures.ThreadPoolExecutor(max_workers=min(8, len(srcs))) as ex:
+        objs = list(ex.map(lambda s: _compile(s, SANITIZE_FLAGS, out_dir), srcs))
+    cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", *SANITIZE_FLAGS, "-o", SANITIZED_LIB, *objs]
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        raise RuntimeError(f"link failed:\n{' '.join(cmd)}\n{res.stdout}\n{res.stderr}")
+    if verbose:
+        print(f"built {SANITIZED_LIB}", file=sys.stderr)
+    return SANITIZED_LIB
+
+
+def asan_runtime() -> str:
+    """Path of the clang ASan runtime that the sanitized library links against."""
+    res = subprocess.run([os.path.join(os.path.dirname(os.path.realpath(HIPCC)), "..", "llvm", "bin", "clang"),
+                          "-print-file-name=libclang_rt.asan-x86_64.so"], capture_output=True, text=True)
+    path = res.stdout.strip()
+    if res.returncode != 0 or not os.path.isabs(path) or not os.path.exists(path):
+        raise RuntimeError("clang ASan runtime not found")
+    return path
 
 
 def clean() -> None:

@@ -18,6 +18,7 @@ namespace {
 thread_local char g_err[512] = "";
 thread_local hipEvent_t g_ev_begin = nullptr;
 thread_local hipEvent_t g_ev_end = nullptr;
+thread_local bool g_checked = false;   // checked mode: validate the record's lists before each launch
 
 calibatt_status_t fail(calibatt_status_t st, const char* fmt, ...) {
   va_list ap;
@@ -107,6 +108,130 @@ calibatt_status_t check_skiplist(const ListView* sl, int32_t H, int32_t N, int32
   if (t < 0 || t >= sl->T || l < 0 || l >= sl->L)
     return fail(CALIBATT_ERR_INVALID_ARG, "record (t=%d, l=%d) outside the dictionary (T=%d, L=%d)", t, l, sl->T,
                 sl->L);
+  return CALIBATT_OK;
+}
+
+// ---- checked mode: validation of a caller's list view on the host ----
+//
+// What the kernels assume of a record's rows and the compile calls guarantee:
+// row pointers non-decreasing (and 0 at the start of a whole dictionary);
+// index lists strictly ascending inside [0, nb); runs lo < hi <= nb, strictly
+// ascending with a gap between neighbours (maximal runs, hence at most
+// ceil(nb/2) per row, the space the kernels stage them in); order, when
+// given, a permutation of [0, nb) per record.
+calibatt_status_t validate_rows(const int64_t* ptr, int64_t row0, int64_t rows, const int32_t* idx,
+                                const uint32_t* runs, int64_t base, int32_t nb) {
+  for (int64_t i = 0; i < rows; ++i) {
+    const int64_t b = ptr[i], e = ptr[i + 1];
+    if (b < 0 || e < b)
+      return fail(CALIBATT_ERR_INVALID_ARG, "row %lld: row pointers %lld .. %lld are not non-decreasing",
+                  (long long)(row0 + i), (long long)b, (long long)e);
+    if (idx) {
+      if (e - b > nb)
+        return fail(CALIBATT_ERR_INVALID_ARG, "row %lld lists %lld key blocks, more than nb = %d",
+                    (long long)(row0 + i), (long long)(e - b), nb);
+      for (int64_t j = b; j < e; ++j) {
+        const int32_t c = idx[j - base];
+        if (c < 0 || c >= nb)
+          return fail(CALIBATT_ERR_INVALID_ARG, "row %lld: key block %d outside [0, %d)", (long long)(row0 + i), c,
+                      nb);
+        if (j > b && c <= idx[j - 1 - base])
+          return fail(CALIBATT_ERR_INVALID_ARG, "row %lld: key blocks not strictly ascending", (long long)(row0 + i));
+      }
+    } else {
+      if (e - b > (nb + 1) / 2)
+        return fail(CALIBATT_ERR_INVALID_ARG, "row %lld holds %lld runs, more than ceil(nb/2) = %d",
+                    (long long)(row0 + i), (long long)(e - b), (nb + 1) / 2);
+      int32_t prev_hi = -1;
+      for (int64_t j = b; j < e; ++j) {
+        const uint32_t w = runs[j - base];
+        const int32_t lo = (int32_t)(w & 0xffffu), hi = (int32_t)(w >> 16);
+        if (!(lo < hi) || hi > nb)
+          return fail(CALIBATT_ERR_INVALID_ARG, "row %lld: run [%d, %d) is empty or reaches past nb = %d",
+                      (long long)(row0 + i), lo, hi, nb);
+        if (lo <= prev_hi)
+          return fail(CALIBATT_ERR_INVALID_ARG, "row %lld: runs not ascending with a gap (run [%d, %d) after %d)",
+                      (long long)(row0 + i), lo, hi, prev_hi);
+        prev_hi = hi;
+      }
+    }
+  }
+  return CALIBATT_OK;
+}
+
+calibatt_status_t validate_order(const int32_t* order, int64_t records, int32_t nb) {
+  std::vector<char> seen(nb);
+  for (int64_t r = 0; r < records; ++r) {
+    std::fill(seen.begin(), seen.end(), 0);
+    for (int32_t i = 0; i < nb; ++i) {
+      const int32_t q = order[r * nb + i];
+      if (q < 0 || q >= nb || seen[q])
+        return fail(CALIBATT_ERR_INVALID_ARG, "order of record %lld is not a permutation of [0, %d)",
+                    (long long)r, nb);
+      seen[q] = 1;
+    }
+  }
+  return CALIBATT_OK;
+}
+
+// Validate the rows of record (t, l) (all heads), or of the whole dictionary
+// when t = l = -1. Device arrays are copied to host memory on `s` first.
+calibatt_status_t validate_view(const ListView* v, int32_t t, int32_t l, bool host_arrays, hipStream_t s) {
+  if (v->T < 1 || v->L < 1 || v->H < 1 || v->N < 1)
+    return fail(CALIBATT_ERR_INVALID_ARG, "view sizes T, L, H and N must be >= 1");
+  if (v->B < 1 || v->nb != ceil_div(v->N, v->B)) return fail(CALIBATT_ERR_INVALID_ARG, "view nb != ceil(N/B)");
+  if (v->nb > CALIBATT_MAX_NB) return fail(CALIBATT_ERR_INVALID_ARG, "nb exceeds %d", CALIBATT_MAX_NB);
+  const bool whole = t == -1 && l == -1;
+  if (!whole && (t < 0 || t >= v->T || l < 0 || l >= v->L))
+    return fail(CALIBATT_ERR_INVALID_ARG, "record (t=%d, l=%d) outside the dictionary (T=%d, L=%d)", t, l, v->T,
+                v->L);
+  const int64_t rec0 = whole ? 0 : ((int64_t)t * v->L + l) * v->H;
+  const int64_t recs = whole ? (int64_t)v->T * v->L * v->H : v->H;
+  const int64_t row0 = rec0 * v->nb, rows = recs * v->nb;
+  std::vector<int64_t> hp;
+  std::vector<int32_t> hi;
+  std::vector<uint32_t> hr;
+  std::vector<int32_t> ho;
+  const int64_t* ptr = v->row_ptr + row0;
+  if (!host_arrays) {
+    hp.resize(rows + 1);
+    hipError_t e = hipMemcpyAsync(hp.data(), ptr, (rows + 1) * sizeof(int64_t), hipMemcpyDeviceToHost, s);
+    if (e == hipSuccess) e = hipStreamSynchronize(s);
+    if (e != hipSuccess) return hip_fail(e, "reading the row pointers");
+    ptr = hp.data();
+  }
+  if (whole && ptr[0] != 0) return fail(CALIBATT_ERR_INVALID_ARG, "row_ptr[0] = %lld, not 0", (long long)ptr[0]);
+  for (int64_t i = 0; i < rows; ++i)
+    if (ptr[i] < 0 || ptr[i + 1] < ptr[i])
+      return fail(CALIBATT_ERR_INVALID_ARG, "row %lld: row pointers %lld .. %lld are not non-decreasing",
+                  (long long)(row0 + i), (long long)ptr[i], (long long)ptr[i + 1]);
+  const int64_t base = ptr[0], count = ptr[rows] - ptr[0];
+  const int32_t* idx = v->col_idx ? v->col_idx + base : nullptr;
+  const uint32_t* runs = v->runs ? v->runs + base : nullptr;
+  const int32_t* order = v->order ? v->order + row0 : nullptr;
+  if (!host_arrays) {
+    hipError_t e = hipSuccess;
+    if (idx && count > 0) {
+      hi.resize(count);
+      e = hipMemcpyAsync(hi.data(), idx, count * sizeof(int32_t), hipMemcpyDeviceToHost, s);
+      idx = hi.data();
+    }
+    if (e == hipSuccess && runs && count > 0) {
+      hr.resize(count);
+      e = hipMemcpyAsync(hr.data(), runs, count * sizeof(uint32_t), hipMemcpyDeviceToHost, s);
+      runs = hr.data();
+    }
+    if (e == hipSuccess && order) {
+      ho.resize(rows);
+      e = hipMemcpyAsync(ho.data(), order, rows * sizeof(int32_t), hipMemcpyDeviceToHost, s);
+      order = ho.data();
+    }
+    if (e == hipSuccess) e = hipStreamSynchronize(s);
+    if (e != hipSuccess) return hip_fail(e, "reading the lists");
+  }
+  calibatt_status_t st = validate_rows(ptr, row0, rows, idx, runs, base, v->nb);
+  if (st != CALIBATT_OK) return st;
+  if (order && (st = validate_order(order, recs, v->nb)) != CALIBATT_OK) return st;
   return CALIBATT_OK;
 }
 
@@ -257,6 +382,7 @@ calibatt_status_t sparse_impl(const void* q, const void* k, const void* v, void*
                               int32_t t, int32_t l, const int32_t* heads, int32_t n_heads, void* stream) {
   calibatt_status_t st = check_skiplist(sl, H, N, t, l);
   if (st != CALIBATT_OK) return st;
+  if (g_checked && (st = validate_view(sl, t, l, false, static_cast<hipStream_t>(stream))) != CALIBATT_OK) return st;
   std::vector<int32_t> hs;
   if ((st = check_heads(heads, n_heads, H, hs)) != CALIBATT_OK) return st;
   calibatt::AttnParams p;
@@ -273,6 +399,7 @@ calibatt_status_t dispatch_impl(const void* q, const void* k, const void* v, voi
   calibatt_status_t st = check_skiplist(sl, H, N, t, l);
   if (st != CALIBATT_OK) return st;
   if (!rep_flags) return fail(CALIBATT_ERR_INVALID_ARG, "rep_flags is NULL");
+  if (g_checked && (st = validate_view(sl, t, l, false, static_cast<hipStream_t>(stream))) != CALIBATT_OK) return st;
   if (H > CALIBATT_MAX_HEADS) return fail(CALIBATT_ERR_INVALID_ARG, "at most %d heads", CALIBATT_MAX_HEADS);
   // Record selection: the flags of (t, l) split the heads into the two paths.
   std::vector<int32_t> sparse_heads, rep_heads;
@@ -304,6 +431,26 @@ int32_t calibatt_version(void) { return 100; }
 void calibatt_set_kernel_events(void* begin, void* end) {
   g_ev_begin = static_cast<hipEvent_t>(begin);
   g_ev_end = static_cast<hipEvent_t>(end);
+}
+
+void calibatt_set_checked_mode(int32_t enabled) { g_checked = enabled != 0; }
+
+calibatt_status_t calibatt_validate_skiplist(const calibatt_skiplist_t* sl, int32_t t, int32_t l,
+                                             int32_t host_arrays, void* stream) {
+  ListView view;
+  calibatt_status_t st = view_of(sl, &view);
+  if (st != CALIBATT_OK) return st;
+  if ((st = validate_view(&view, t, l, host_arrays != 0, static_cast<hipStream_t>(stream))) != CALIBATT_OK) return st;
+  return ok();
+}
+
+calibatt_status_t calibatt_validate_intervals(const calibatt_intervals_t* il, int32_t t, int32_t l,
+                                              int32_t host_arrays, void* stream) {
+  ListView view;
+  calibatt_status_t st = view_of(il, &view);
+  if (st != CALIBATT_OK) return st;
+  if ((st = validate_view(&view, t, l, host_arrays != 0, static_cast<hipStream_t>(stream))) != CALIBATT_OK) return st;
+  return ok();
 }
 
 calibatt_status_t calibatt_compile_skiplist(const uint8_t* masks, int32_t T, int32_t L, int32_t H, int32_t N,

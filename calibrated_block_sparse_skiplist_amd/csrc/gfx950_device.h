@@ -95,12 +95,18 @@ __device__ __forceinline__ int64_t xcd_item_after(int64_t b, int64_t total, int 
 // operand wait into lgkmcnt(0), serialising the MFMA operand reads. The
 // hardware counts these copies in vmcnt only; the kernel waits for them
 // explicitly (wait_vmcnt) before the barrier that publishes a stage. The
-// statement has no register outputs, M0 is set inside it, and the memory
-// clobber keeps it after the barrier that frees the destination buffer.
+// statement has no register outputs, M0 is set inside it (and declared
+// clobbered, so the compiler keeps no value of its own in M0 across it), and
+// the memory clobber keeps it after the barrier that frees the destination
+// buffer. (clang warns about any clobber of M0, a register it reserves; the
+// declaration is what is wanted here.)
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
 __device__ __forceinline__ void dma16(const char* base, uint32_t off, uint4* lds) {
   const uint32_t m0 = (uint32_t)(uintptr_t)(lds_void*)lds;
-  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2" :: "s"(m0), "v"(off), "s"(base) : "memory");
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2" :: "s"(m0), "v"(off), "s"(base) : "memory", "m0");
 }
+#pragma clang diagnostic pop
 
 }  // namespace dev
 }  // namespace calibatt

@@ -19,9 +19,9 @@
  * Conventions shared by every entry point
  *  - All array pointers are device pointers (hipMalloc / torch CUDA tensors)
  *    unless marked "host". The caller owns every buffer; the library never
- *    frees caller memory and keeps no state between calls beyond two
- *    thread-local items: the last error message and a pending
- *    calibatt_set_kernel_events pair.
+ *    frees caller memory and keeps no state between calls beyond three
+ *    thread-local items: the last error message, a pending
+ *    calibatt_set_kernel_events pair and the checked-mode switch.
  *  - Tensors Q, K, V, O are [H][N][d], contiguous, row-major. Token order is
  *    n = (f*R + r)*C + c: frame f, spatial row r, column c.
  *  - Blocks: query/key block b covers tokens [b*B, min((b+1)*B, N));
@@ -57,7 +57,11 @@ typedef enum {
   CALIBATT_ERR_UNSUPPORTED = 4
 } calibatt_status_t;
 
-typedef enum { CALIBATT_BF16 = 0, CALIBATT_F32 = 1 } calibatt_dtype_t;
+/* Element type of Q, K, V and O. A plain 32-bit integer (an enum's size and
+ * range are not fixed across C and C++): a value other than the two below is
+ * rejected with CALIBATT_ERR_INVALID_ARG. */
+typedef int32_t calibatt_dtype_t;
+enum { CALIBATT_BF16 = 0, CALIBATT_F32 = 1 };
 
 /* Limits of one call. */
 #define CALIBATT_MAX_HEADS 256    /* heads taking part in one attention call */
@@ -222,6 +226,43 @@ calibatt_status_t calibatt_layer_dispatch_iv(const void* q, const void* k, const
                                              const calibatt_intervals_t* il, int32_t t, int32_t l,
                                              const uint8_t* rep_flags, int32_t F, int32_t R, int32_t C,
                                              const int32_t* anchor_rows, int32_t k_anchors, void* stream);
+
+/*
+ * ---- Checked mode (for list views the caller built or loaded itself) ----
+ *
+ * The attention calls trust a view's contents: the compile calls produce
+ * valid lists ([Notes] Key Design 4: the lists are compiled once, offline, and
+ * read-only at inference), and a malformed view makes the kernels read outside
+ * the key blocks or their list staging. These calls check a view on the host.
+ *
+ * calibatt_validate_skiplist / calibatt_validate_intervals: validate the rows
+ * of record (t, l), all H heads of it, or of the whole dictionary when
+ * t = l = -1:
+ *   - row pointers non-decreasing (row_ptr[0] = 0 for the whole dictionary);
+ *   - index lists: entries strictly ascending inside [0, nb);
+ *   - runs: lo < hi <= nb, strictly ascending with a gap of at least one
+ *     block between neighbours (maximal runs, at most ceil(nb/2) per row);
+ *   - order (when not NULL): a permutation of [0, nb) per record.
+ * host_arrays = 0: the view's arrays are device memory; they are copied to
+ * host memory on `stream`, which is synchronised. host_arrays != 0: they are
+ * host memory and no HIP call is made (stream ignored).
+ * Returns CALIBATT_OK, or CALIBATT_ERR_INVALID_ARG with the first offending
+ * row named in calibatt_last_error() (CALIBATT_ERR_HIP if a copy fails).
+ */
+calibatt_status_t calibatt_validate_skiplist(const calibatt_skiplist_t* sl, int32_t t, int32_t l,
+                                             int32_t host_arrays, void* stream);
+calibatt_status_t calibatt_validate_intervals(const calibatt_intervals_t* il, int32_t t, int32_t l,
+                                              int32_t host_arrays, void* stream);
+
+/*
+ * Checked mode for this thread: when enabled, calibatt_block_sparse_attn(_iv)
+ * and calibatt_layer_dispatch(_iv) validate the record (t, l) they are given,
+ * as calibatt_validate_* does (copying its lists to host memory and
+ * synchronising `stream`), before anything is enqueued; a malformed record
+ * returns CALIBATT_ERR_INVALID_ARG and no kernel runs. Off by default (the
+ * calls then stay fully asynchronous).
+ */
+void calibatt_set_checked_mode(int32_t enabled);
 
 /*
  * ---- Offline calibration (produces the masks compiled above) ----

@@ -244,3 +244,130 @@ def test_product_path_does_not_import_the_oracle():
             if f.endswith((".py", ".hip", ".h", ".cpp")):
                 src = open(os.path.join(dirpath, f)).read()
                 assert not re.search(r"\boracle\b", src.replace("the oracle", "")), f
+
+
+# ---------------------------------------------------------------------------
+# Checked mode: host-side validation of list views (host arrays: no HIP call)
+# ---------------------------------------------------------------------------
+def _host_lists(T=2, L=2, H=3, N=1000, B=128, p=0.4, seed=0):
+    import oracle
+    nb = -(-N // B)
+    rng = np.random.default_rng(seed)
+    masks = (rng.random((T, L, H, nb, nb)) < p).astype(np.uint8)
+    masks[0, 0, 1, 2] = 0                      # an empty row
+    rp, ci, order = oracle.compile_skiplist(masks)
+    iv_ptr, iv, _ = oracle.compile_intervals(masks)
+    packed = (iv[:, 0].astype(np.int64) | (iv[:, 1].astype(np.int64) << 16)).astype(np.uint32)
+    return dict(T=T, L=L, H=H, N=N, B=B, nb=nb, rp=rp.astype(np.int64), ci=ci.astype(np.int32),
+                order=order.astype(np.int32), iv_ptr=iv_ptr.astype(np.int64), iv=packed)
+
+
+def _validate_csr(d, rp=None, ci=None, order="keep", t=-1, l=-1):
+    rp = d["rp"] if rp is None else rp
+    ci = d["ci"] if ci is None else ci
+    order = d["order"] if isinstance(order, str) else order
+    view = cal.SkipListView(d["T"], d["L"], d["H"], d["N"], d["B"], d["nb"], rp.ctypes.data,
+                            ci.ctypes.data if ci.size else P, order.ctypes.data if order is not None else None)
+    return lib.calibatt_validate_skiplist(ctypes.byref(view), t, l, 1, None)
+
+
+def _validate_runs(d, ptr=None, iv=None, t=-1, l=-1):
+    ptr = d["iv_ptr"] if ptr is None else ptr
+    iv = d["iv"] if iv is None else iv
+    view = cal.IntervalListView(d["T"], d["L"], d["H"], d["N"], d["B"], d["nb"], ptr.ctypes.data,
+                                iv.ctypes.data, d["order"].ctypes.data)
+    return lib.calibatt_validate_intervals(ctypes.byref(view), t, l, 1, None)
+
+
+def test_validate_accepts_compiled_lists():
+    d = _host_lists()
+    assert _validate_csr(d) == cal.OK, cal.last_error()
+    assert _validate_csr(d, order=None) == cal.OK
+    assert _validate_runs(d) == cal.OK, cal.last_error()
+    for t in range(d["T"]):
+        for l in range(d["L"]):
+            assert _validate_csr(d, t=t, l=l) == cal.OK
+            assert _validate_runs(d, t=t, l=l) == cal.OK
+
+
+def _row_with(d, ptr_key, min_len):
+    ptr = d[ptr_key]
+    lens = np.diff(ptr)
+    return int(np.flatnonzero(lens >= min_len)[0])
+
+
+@pytest.mark.parametrize("case", ["out_of_range", "negative", "descending", "duplicate", "row_ptr_down",
+                                  "row_ptr_start", "order_repeat", "order_range"])
+def test_validate_rejects_bad_index_lists(case):
+    d = _host_lists()
+    rp, ci, order = d["rp"].copy(), d["ci"].copy(), d["order"].copy()
+    row = _row_with(d, "rp", 2)
+    j = int(rp[row])
+    if case == "out_of_range":
+        ci[j + 1] = d["nb"]
+    elif case == "negative":
+        ci[j] = -1
+    elif case == "descending":
+        ci[j], ci[j + 1] = ci[j + 1], ci[j]
+    elif case == "duplicate":
+        ci[j + 1] = ci[j]
+    elif case == "row_ptr_down":
+        rp[row + 1] = rp[row] - 1
+    elif case == "row_ptr_start":
+        rp[:] += 1
+    elif case == "order_repeat":
+        order[1] = order[0]
+    else:
+        order[5] = d["nb"]
+    assert _validate_csr(d, rp=rp, ci=ci, order=order) == INVALID
+    assert cal.last_error()
+    # the record holding the bad row is rejected, a record before it is not (where there is one)
+    rec = row // d["nb"] if case not in ("order_repeat", "order_range", "row_ptr_start") else 0
+    t, l = divmod(rec // d["H"], d["L"])
+    assert _validate_csr(d, rp=rp, ci=ci, order=order, t=t, l=l) == INVALID or case == "row_ptr_start"
+
+
+@pytest.mark.parametrize("case", ["empty", "past_nb", "overlap", "adjacent", "descending", "too_many"])
+def test_validate_rejects_bad_runs(case):
+    d = _host_lists(p=0.3)
+    ptr, iv = d["iv_ptr"].copy(), d["iv"].copy()
+    row = _row_with(d, "iv_ptr", 2)
+    j = int(ptr[row])
+    lo0, hi0 = int(iv[j] & 0xffff), int(iv[j] >> 16)
+    lo1, hi1 = int(iv[j + 1] & 0xffff), int(iv[j + 1] >> 16)
+    pack = lambda lo, hi: np.uint32(lo | (hi << 16))
+    if case == "empty":
+        iv[j] = pack(lo0, lo0)
+    elif case == "past_nb":
+        iv[j + 1] = pack(lo1, d["nb"] + 1)
+    elif case == "overlap":
+        iv[j + 1] = pack(hi0 - 1, hi1)
+    elif case == "adjacent":
+        iv[j + 1] = pack(hi0, hi1)
+    elif case == "descending":
+        iv[j], iv[j + 1] = iv[j + 1], iv[j]
+    else:
+        # every block of a row as its own one-block run: more runs than ceil(nb/2)
+        nb = d["nb"]
+        new_ptr = ptr.copy()
+        extra = nb - (ptr[row + 1] - ptr[row])
+        new_ptr[row + 1:] += extra
+        iv = np.concatenate([iv[:j], np.array([pack(c, c + 1) for c in range(nb)], np.uint32), iv[ptr[row + 1]:]])
+        ptr = new_ptr
+    assert _validate_runs(d, ptr=ptr, iv=iv) == INVALID
+    assert cal.last_error()
+
+
+def test_validate_rejects_bad_view_sizes():
+    d = _host_lists()
+    assert _validate_csr(d, t=2, l=0) == INVALID and "outside the dictionary" in cal.last_error()
+    assert _validate_csr(d, t=0, l=-1) == INVALID
+    d2 = dict(d, nb=d["nb"] + 1)
+    assert _validate_csr(d2) == INVALID and "nb" in cal.last_error()
+    assert lib.calibatt_validate_skiplist(None, -1, -1, 1, None) == INVALID
+
+
+def test_checked_mode_switch():
+    # the switch is thread-local state; toggling it makes no HIP call
+    lib.calibatt_set_checked_mode(1)
+    lib.calibatt_set_checked_mode(0)

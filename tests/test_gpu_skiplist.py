@@ -102,3 +102,51 @@ def test_size_query_and_capacity_error():
     assert torch.all(small == -5)          # nothing written on CAPACITY
     want_rp, _, _ = oracle.compile_skiplist(masks)
     np.testing.assert_array_equal(rp.cpu().numpy(), want_rp)
+
+
+def test_checked_mode_on_device_views():
+    """Compiled device views validate; in checked mode a malformed record is rejected before any launch
+    (the output stays untouched) and a valid one gives the same output as without checking. The
+    malformed list only reorders valid key blocks, so even an unchecked launch would stay in bounds."""
+    from _gpu_util import alloc_out, random_qkv, to_device
+    H, N, d, B = 3, 1000, 128, 128
+    nb = -(-N // B)
+    rng = np.random.default_rng(41)
+    masks = (rng.random((1, 2, H, nb, nb)) < 0.5).astype(np.uint8)
+    for l in range(2):
+        for h in range(H):
+            np.fill_diagonal(masks[0, l, h], 1)
+    dm = torch.from_numpy(masks).cuda()
+    sl = cal.compile_skiplist(dm, N, B)
+    il = cal.compile_intervals(dm, N, B)
+    cal.calibatt_validate_skiplist(sl)
+    cal.calibatt_validate_skiplist(sl, 0, 1)
+    cal.calibatt_validate_intervals(il)
+    cal.calibatt_validate_intervals(il, 0, 0)
+    q, k, v = (to_device(x, "bf16") for x in random_qkv(H, N, d, "bf16", seed=42))
+    o_ref, _ = alloc_out(H, N, d, "bf16")
+    cal.calibatt_block_sparse_attn(q, k, v, o_ref, None, sl, 0, 1)
+    # a descending pair of key blocks in a row of record (0, 1)
+    rp = sl.row_ptr.cpu().numpy()
+    lens = np.diff(rp)
+    row = H * nb + int(np.flatnonzero(lens[H * nb:] >= 2)[0])
+    bad_ci = sl.col_idx.clone()
+    j = int(rp[row])
+    bad_ci[j], bad_ci[j + 1] = sl.col_idx[j + 1].item(), sl.col_idx[j].item()
+    bad = cal.SkipList(sl.T, sl.L, sl.H, sl.N, sl.B, sl.nb, sl.row_ptr, bad_ci, sl.order, sl.nnz)
+    with pytest.raises(cal.CalibattError, match="ascending"):
+        cal.calibatt_validate_skiplist(bad, 0, 1)
+    cal.calibatt_validate_skiplist(bad, 0, 0)          # the other record is fine
+    cal.calibatt_set_checked_mode(True)
+    try:
+        o, _ = alloc_out(H, N, d, "bf16")
+        with pytest.raises(cal.CalibattError, match="ascending"):
+            cal.calibatt_block_sparse_attn(q, k, v, o, None, bad, 0, 1)
+        torch.cuda.synchronize()
+        assert torch.isnan(o.float()).all(), "a rejected call wrote its output"
+        o2, _ = alloc_out(H, N, d, "bf16")
+        cal.calibatt_block_sparse_attn(q, k, v, o2, None, sl, 0, 1)
+        torch.cuda.synchronize()
+        assert torch.equal(o2.view(torch.int16), o_ref.view(torch.int16))
+    finally:
+        cal.calibatt_set_checked_mode(False)

@@ -76,3 +76,13 @@ def test_dictionary_workload_small():
     assert abs(s - 0.68) < 0.01
     _, dense, _ = workloads.make_dictionary_workload(0.0, 0.0, L=1, H=2)
     assert dense.min() == 1
+
+
+def test_dictionary_prefix_of_layers():
+    # The benchmark's sweep summary times the first layers of each dictionary point, drawn with
+    # L = 2; they must be the first two layers of the full 40-layer dictionary.
+    for sp, rf in ((0.68, 0.25), (0.85, 0.10)):
+        _, m40, f40 = workloads.make_dictionary_workload(sp, rf)
+        _, m2, f2 = workloads.make_dictionary_workload(sp, rf, L=2)
+        np.testing.assert_array_equal(m40[:, :2], m2)
+        np.testing.assert_array_equal(f40[:, :2], f2)
