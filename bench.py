@@ -209,14 +209,16 @@ def cpu_baseline(wl, budget_s: float, flops_layer: float):
     flop = sum(r[0] for r in res)
     rate = sum(r[0] / r[1] for r in res if r[1] > 0)
     done = sum(r[2] for r in res)
+    busy = max(r[1] for r in res)
     n_sp = sum(1 for u in units if u[0] == "sparse")
     value = rate / 1e12 if rate > 0 else None
     return {"value": value, "unit": "TFLOP/s", "cores": workers, "kind": "oracle",
             "sample": f"fp64 numpy oracle, process pool of {workers} workers (BLAS 1 thread each) over heads "
                       f"{sub_sparse} (block-sparse) and {sub_rep} (anchor) of the same layer: {done} of "
-                      f"{len(units)} units ({n_sp} query blocks, {len(units) - n_sp} anchor frames) in "
-                      f"{budget_s:.0f} s per worker, {flop / 1e12:.3f} TFLOP; the full layer extrapolated by "
-                      f"algorithmic FLOP",
+                      f"{len(units)} units ({n_sp} query blocks, {len(units) - n_sp} anchor frames), "
+                      f"{flop / 1e12:.3f} TFLOP, in at most {busy:.1f} s per worker (budget {budget_s:.0f} s); "
+                      f"the full layer extrapolated by algorithmic FLOP",
+            "seconds_busy_max": round(busy, 2), "units_done": done, "units_total": len(units),
             "cores_visible": cores_visible, "blas_threads_per_worker": 1,
             "subset_heads": {"block_sparse": sub_sparse, "anchor": sub_rep},
             "extrapolated": True,
