@@ -13,6 +13,7 @@ The names follow the C ABI in include/calibatt.h:
   similarity to the nearest anchor row, and the per-head repetition flags
 * ``calibatt_validate_skiplist`` / ``calibatt_validate_intervals`` / ``calibatt_set_checked_mode`` --
   checked mode: host-side validation of a list view before it reaches the kernels
+* ``calibatt_block_energy_noalloc`` -- block energies for callers that cannot allocate device memory
 
 All computation happens in the library's HIP kernels; this package only
 marshals arguments. Importing it fails if the library has not been built.
@@ -24,6 +25,7 @@ from ._lib import (BF16, F32, CalibattError, IntervalList, IntervalListView, Ski
                    calibatt_layer_dispatch_iv, calibatt_repetition_flags, calibatt_set_kernel_events,
                    calibatt_spatial_similarity, calibatt_version,
                    calibatt_validate_skiplist, calibatt_validate_intervals, calibatt_set_checked_mode,
+                   calibatt_block_energy_noalloc,
                    compile_intervals, compile_skiplist, energy_work_bytes, last_error)
 
 __all__ = ["BF16", "F32", "CalibattError", "IntervalList", "IntervalListView", "SkipList", "SkipListView",
@@ -33,4 +35,5 @@ __all__ = ["BF16", "F32", "CalibattError", "IntervalList", "IntervalListView", "
            "calibatt_layer_dispatch_iv", "calibatt_repetition_flags", "calibatt_set_kernel_events",
            "calibatt_spatial_similarity", "calibatt_version",
            "calibatt_validate_skiplist", "calibatt_validate_intervals", "calibatt_set_checked_mode",
+           "calibatt_block_energy_noalloc",
            "compile_intervals", "compile_skiplist", "energy_work_bytes", "last_error"]

@@ -29,7 +29,9 @@ EXPORTED = (
     "calibatt_spatial_similarity", "calibatt_repetition_flags",
     "calibatt_last_error", "calibatt_set_kernel_events", "calibatt_version",
     "calibatt_validate_skiplist", "calibatt_validate_intervals", "calibatt_set_checked_mode",
+    "calibatt_block_energy_noalloc",
 )
+NOALLOC_SCRATCH_BYTES = 256 << 20
 
 
 class CalibattError(RuntimeError):
@@ -107,6 +109,8 @@ def _load():
     lib.calibatt_validate_intervals.restype = i32
     lib.calibatt_set_checked_mode.argtypes = [i32]
     lib.calibatt_set_checked_mode.restype = None
+    lib.calibatt_block_energy_noalloc.argtypes = [vp, vp, i32, i32, i32, i32, f32, i32, vp, vp, i32, vp]
+    lib.calibatt_block_energy_noalloc.restype = i32
     return lib
 
 
@@ -333,6 +337,17 @@ def calibatt_block_energy(q, k, energy, B: int, heads=None, scale: float | None 
     _check(lib.calibatt_block_energy(_ptr(q), _ptr(k), H, N, d, _dtype_code(q), scale, B, _ptr(energy),
                                      harr.ctypes.data if harr is not None else None, nh, _ptr(work), wbytes,
                                      _stream(stream)))
+
+
+def calibatt_block_energy_noalloc(q, k, energy, B: int, heads=None, scale: float | None = None,
+                                  stream=None) -> None:
+    """calibatt_block_energy for callers that cannot allocate: the workspace is the library's own
+    per-GPU scratch (calls overlapping on one GPU race)."""
+    H, N, d = q.shape
+    scale = float(np.float32(1.0 / np.sqrt(d))) if scale is None else scale
+    harr, nh = _host_i32(heads)
+    _check(lib.calibatt_block_energy_noalloc(_ptr(q), _ptr(k), H, N, d, _dtype_code(q), scale, B, _ptr(energy),
+                                             harr.ctypes.data if harr is not None else None, nh, _stream(stream)))
 
 
 def calibatt_select_blocks(energy, tau: float, mask=None, counts=None, stream=None) -> None:

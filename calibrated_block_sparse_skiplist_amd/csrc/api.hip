@@ -9,9 +9,19 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <vector>
 
 #include "internal.h"
+
+// Device scratch of calibatt_block_energy_noalloc (CALIBATT_NOALLOC_SCRATCH_BYTES,
+// include/calibatt.h): the one-pass energy workspace for callers that cannot
+// allocate device memory. Each GPU the
+// library runs on holds its own copy from the module's load until the process
+// ends. Host code never uses the name `scratch` as an address (on the host it
+// is only a stand-in): scratch_on_current_device() looks the device address
+// up once per device with hipGetSymbolAddress and every launch takes that.
+static __device__ __align__(256) float scratch[CALIBATT_NOALLOC_SCRATCH_BYTES / sizeof(float)];
 
 namespace {
 
@@ -247,6 +257,50 @@ calibatt_status_t check_anchors(int32_t N, int32_t F, int32_t R, int32_t C, cons
     if (i > 0 && anchors[i] <= anchors[i - 1])
       return fail(CALIBATT_ERR_INVALID_ARG, "anchor rows must be strictly ascending");
   }
+  return CALIBATT_OK;
+}
+
+// Device address of `scratch` on the current device, looked up once per device
+// (with that device current) and kept.
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+hipError_t scratch_on_current_device(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (!ptr) return hipErrorInvalidSymbol;
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return hipSuccess;
+}
+
+// check_heads without heap use: distinct heads in [0, H), at most CALIBATT_MAX_HEADS, into out[].
+calibatt_status_t check_heads_fixed(const int32_t* heads, int32_t n_heads, int32_t H, int32_t* out, int32_t* n_out) {
+  if (!heads) {
+    if (H > CALIBATT_MAX_HEADS) return fail(CALIBATT_ERR_INVALID_ARG, "at most %d heads per call", CALIBATT_MAX_HEADS);
+    for (int32_t h = 0; h < H; ++h) out[h] = h;
+    *n_out = H;
+    return CALIBATT_OK;
+  }
+  if (n_heads < 0) return fail(CALIBATT_ERR_INVALID_ARG, "n_heads must be >= 0");
+  if (n_heads > CALIBATT_MAX_HEADS) return fail(CALIBATT_ERR_INVALID_ARG, "at most %d heads per call", CALIBATT_MAX_HEADS);
+  for (int32_t i = 0; i < n_heads; ++i) {
+    const int32_t h = heads[i];
+    if (h < 0 || h >= H) return fail(CALIBATT_ERR_INVALID_ARG, "head index %d out of range [0, %d)", h, H);
+    for (int32_t j = 0; j < i; ++j)
+      if (out[j] == h) return fail(CALIBATT_ERR_INVALID_ARG, "head index %d listed twice", h);
+    out[i] = h;
+  }
+  *n_out = n_heads;
   return CALIBATT_OK;
 }
 
@@ -576,6 +630,67 @@ calibatt_status_t calibatt_block_energy(const void* q, const void* k, int32_t H,
     p.n_heads = (int32_t)(h1 - h0);
     for (size_t i = h0; i < h1; ++i) p.heads[i - h0] = hs[i];
     if ((e = calibatt::launch_energy(p, d, B, s)) != hipSuccess) return hip_fail(e, "block energy kernel launch");
+  }
+  if (ee && (e = hipEventRecord(ee, s)) != hipSuccess) return hip_fail(e, "hipEventRecord");
+  return ok();
+}
+
+calibatt_status_t calibatt_block_energy_noalloc(const void* q, const void* k, int32_t H, int32_t N, int32_t d,
+                                                calibatt_dtype_t dtype, float scale, int32_t B, float* energy,
+                                                const int32_t* heads, int32_t n_heads, void* stream) {
+  calibatt_status_t st = check_tensors(q, k, q, energy, H, N, d, dtype, scale);
+  if (st != CALIBATT_OK) return st;
+  if (B != 64 && B != 128) return fail(CALIBATT_ERR_INVALID_ARG, "block size %d is not supported", B);
+  const int64_t nb = ceil_div(N, B);
+  if (nb > CALIBATT_MAX_NB) return fail(CALIBATT_ERR_INVALID_ARG, "nb exceeds %d", CALIBATT_MAX_NB);
+  int32_t hs[CALIBATT_MAX_HEADS];
+  int32_t nh = 0;
+  if ((st = check_heads_fixed(heads, n_heads, H, hs, &nh)) != CALIBATT_OK) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e;
+  if (s) {
+    int cur = -1, sdev = -1;
+    if ((e = hipGetDevice(&cur)) != hipSuccess) return hip_fail(e, "hipGetDevice");
+    if ((e = hipStreamGetDevice(s, &sdev)) != hipSuccess) return hip_fail(e, "hipStreamGetDevice");
+    if (sdev != cur)
+      return fail(CALIBATT_ERR_INVALID_ARG, "stream is on device %d, the current device is %d", sdev, cur);
+  }
+  // one query block's workspace: nb * B floats; a launch holds as many as the scratch does
+  const int64_t per_item = nb * B * (int64_t)sizeof(float);
+  if (dtype == CALIBATT_BF16 && per_item > (int64_t)CALIBATT_NOALLOC_SCRATCH_BYTES)
+    return fail(CALIBATT_ERR_CAPACITY, "a query block's workspace (%lld bytes) exceeds the scratch (%llu bytes)",
+                (long long)per_item, (unsigned long long)CALIBATT_NOALLOC_SCRATCH_BYTES);
+  calibatt::EnergyParams p;
+  std::memset(&p, 0, sizeof(p));
+  p.q = q;
+  p.k = k;
+  p.energy = energy;
+  p.head_stride = (int64_t)N * d;
+  p.N = N;
+  p.nb = (int32_t)nb;
+  p.scale = scale;
+  p.scale_log2 = scale * 1.4426950408889634f;
+  p.dtype_f32 = dtype == CALIBATT_F32 ? 1 : 0;
+  p.n_heads = nh;
+  for (int32_t i = 0; i < nh; ++i) p.heads[i] = hs[i];
+  if (dtype == CALIBATT_BF16) {
+    void* ptr = nullptr;
+    if ((e = scratch_on_current_device(&ptr)) != hipSuccess) return hip_fail(e, "device scratch lookup");
+    p.work = static_cast<float*>(ptr);
+  }
+  hipEvent_t eb = g_ev_begin, ee = g_ev_end;
+  g_ev_begin = g_ev_end = nullptr;
+  if (eb && (e = hipEventRecord(eb, s)) != hipSuccess) return hip_fail(e, "hipEventRecord");
+  if (dtype == CALIBATT_BF16) {
+    const int64_t total = (int64_t)nh * nb;
+    const int64_t cap = (int64_t)CALIBATT_NOALLOC_SCRATCH_BYTES / per_item;
+    for (int64_t i0 = 0; i0 < total; i0 += cap) {
+      p.item0 = i0;
+      if ((e = calibatt::launch_energy_onepass_items(p, d, B, std::min(cap, total - i0), s)) != hipSuccess)
+        return hip_fail(e, "block energy kernel launch");
+    }
+  } else if ((e = calibatt::launch_energy(p, d, B, s)) != hipSuccess) {
+    return hip_fail(e, "block energy kernel launch");
   }
   if (ee && (e = hipEventRecord(ee, s)) != hipSuccess) return hip_fail(e, "hipEventRecord");
   return ok();

@@ -244,7 +244,8 @@ __global__ __launch_bounds__(BLK * 2) void energy_bf16_kernel(const EnergyParams
 }
 
 // One pass with a workspace p.work of [items][nb][BLK] floats (item = index
-// of the head in p.heads * nb + query block). The two key-half lanes of a
+// of the head in p.heads * nb + query block; the launch's items from p.item0
+// on, the first at p.work). The two key-half lanes of a
 // query share a lazily moved reference maximum m; at the end of key block c,
 // lane h = 0 stores log2(sum over the block of exp2(s - m)) + (m - m0), m0 the
 // reference after the first stage. With the query's total
@@ -275,12 +276,13 @@ __global__ __launch_bounds__(BLK * 2) void energy_bf16_onepass_kernel(const Ener
   float scale_log2 = p.scale_log2;
   asm volatile("" : "+s"(n_tok), "+s"(scale_log2));
 
-  const int64_t item = xcd_item(blockIdx.x, gridDim.x, 32);
+  const int64_t local = xcd_item(blockIdx.x, gridDim.x, 32);
+  const int64_t item = p.item0 + local;
   const int head = p.heads[item / nb];
   const int r = (int)(item % nb);
   const u16* Q = static_cast<const u16*>(p.q) + (int64_t)head * p.head_stride;
   const char* Kb = reinterpret_cast<const char*>(static_cast<const u16*>(p.k) + (int64_t)head * p.head_stride);
-  float* ws = p.work + item * (int64_t)nb * BLK;
+  float* ws = p.work + local * (int64_t)nb * BLK;
 
   const int qtok = r * BLK + wave * 32 + l32;
   const bool q_ok = qtok < n_tok;
@@ -589,9 +591,29 @@ hipError_t launch_energy_typed(const EnergyParams& p, hipStream_t s) {
   return hipGetLastError();
 }
 
+// The one-pass bf16 kernel over items [p.item0, p.item0 + n_items) (a launch
+// whose workspace holds fewer items than the heads have).
+template <int D, int BLK>
+hipError_t launch_energy_onepass_typed(const EnergyParams& p, int64_t n_items, hipStream_t s) {
+  if (n_items == 0) return hipSuccess;
+  hipLaunchKernelGGL((energy_bf16_onepass_kernel<D, BLK>), dim3((unsigned)n_items), dim3(BLK * 2), 0, s, p);
+  return hipGetLastError();
+}
+
 }  // namespace
 
+hipError_t launch_energy_onepass_items(const EnergyParams& p, int d, int blk, int64_t n_items, hipStream_t s) {
+  if (!p.work || p.dtype_f32 || n_items < 0 || p.item0 < 0 || p.item0 + n_items > (int64_t)p.n_heads * p.nb)
+    return hipErrorInvalidValue;
+  if (d == 128 && blk == 128) return launch_energy_onepass_typed<128, 128>(p, n_items, s);
+  if (d == 64 && blk == 128) return launch_energy_onepass_typed<64, 128>(p, n_items, s);
+  if (d == 128 && blk == 64) return launch_energy_onepass_typed<128, 64>(p, n_items, s);
+  if (d == 64 && blk == 64) return launch_energy_onepass_typed<64, 64>(p, n_items, s);
+  return hipErrorInvalidValue;
+}
+
 hipError_t launch_energy(const EnergyParams& p, int d, int blk, hipStream_t s) {
+  if (p.item0 != 0) return hipErrorInvalidValue;   // whole heads per launch
   if (d == 128 && blk == 128) return launch_energy_typed<128, 128>(p, s);
   if (d == 64 && blk == 128) return launch_energy_typed<64, 128>(p, s);
   if (d == 128 && blk == 64) return launch_energy_typed<128, 64>(p, s);

@@ -71,12 +71,15 @@ struct BcastParams {
 };
 
 // Block energies of selected heads for one prompt: one work item per
-// (head, query block) in head-major order.
+// (head, query block) in head-major order; a launch covers the items
+// [item0, item0 + grid size).
 struct EnergyParams {
   const void* q;
   const void* k;
   float* energy;            // [H][nb][nb]
-  float* work;              // bf16 one-pass kernel: [n_heads][nb][nb][B] floats, or null (two passes)
+  float* work;              // bf16 one-pass kernel: [items][nb][B] floats, or null (two passes)
+  int64_t item0;            // first item of the launch (item = head index in heads * nb + query block);
+                            // the workspace holds the launch's items from item0 on
   int64_t head_stride;      // N * d elements
   int32_t N;
   int32_t nb;
@@ -119,6 +122,7 @@ hipError_t launch_attn_bf16(const AttnParams& p, int d, int blk, hipStream_t s);
 hipError_t launch_attn_f32(const AttnParams& p, int d, int blk, hipStream_t s);
 hipError_t launch_broadcast(const BcastParams& p, hipStream_t s);
 hipError_t launch_energy(const EnergyParams& p, int d, int blk, hipStream_t s);
+hipError_t launch_energy_onepass_items(const EnergyParams& p, int d, int blk, int64_t n_items, hipStream_t s);
 hipError_t launch_similarity(const SimParams& p, int d, bool f32, hipStream_t s);
 hipError_t launch_rep_flags(const float* sims, int P, int H, int F, int R, const RepFlagParams& q, uint8_t* flags,
                             float* mean, hipStream_t s);

@@ -294,6 +294,28 @@ calibatt_status_t calibatt_block_energy(const void* q, const void* k, int32_t H,
                                         void* stream);
 
 /*
+ * calibatt_block_energy for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving or calibration loops, harnesses that
+ * forbid hipMalloc): the same energies, bitwise equal to calibatt_block_energy
+ * with a workspace, with the one-pass workspace taken from a scratch array the
+ * library holds on each GPU (CALIBATT_NOALLOC_SCRATCH_BYTES = 256 MiB, held from
+ * the first call on a device until the process ends). The listed heads' query
+ * blocks run in launches of as many as the scratch holds (nb*B floats each:
+ * 887 query blocks per launch at N = 75,600, B = 128; every supported shape
+ * fits at least one). No device memory is allocated or freed, and no host heap
+ * is used. Arguments and results as calibatt_block_energy (fp32 inputs take the
+ * two-pass fp32 kernel, which needs no workspace). `stream` must belong to the
+ * current device. Calls that overlap on one GPU (other streams or threads)
+ * share its scratch and race: serialise them. Returns CALIBATT_ERR_CAPACITY if
+ * one query block's workspace exceeds the scratch (not reachable with
+ * nb <= CALIBATT_MAX_NB).
+ */
+#define CALIBATT_NOALLOC_SCRATCH_BYTES (256ull << 20)
+calibatt_status_t calibatt_block_energy_noalloc(const void* q, const void* k, int32_t H, int32_t N, int32_t d,
+                                                calibatt_dtype_t dtype, float scale, int32_t B, float* energy,
+                                                const int32_t* heads, int32_t n_heads, void* stream);
+
+/*
  * Per-prompt selection ([Notes] Key Design 1): for every row of `energy`
  * (rows x nb, device, finite and >= 0), sort the energies in descending order
  * (ties to the lower key block) and keep the shortest prefix whose cumulative
