@@ -319,12 +319,11 @@ void fill_common(calibatt::AttnParams& p, const void* q, const void* k, const vo
   p.scale_log2 = scale * 1.4426950408889634f;
   // Work order: query blocks in block order (neighbours share key blocks), in
   // runs of 32 consecutive items per XCD; heaviest-first order per record
-  // (the compiled `order`) measured no faster on the Wan-shaped layers. Each
-  // XCD's share of the grid is fixed by the round-robin dispatch, so when runs
-  // cover whole heads (nb divides or is a multiple of 8*32) the chunks turn
-  // per run: otherwise an XCD would take the same, lighter or heavier, slice
-  // of every head.
-  p.use_order = 0;
+  // (the compiled `order`) measured no faster on the Wan-shaped layers, so the
+  // kernels do not read it. Each XCD's share of the grid is fixed by the
+  // round-robin dispatch, so when runs cover whole heads (nb divides or is a
+  // multiple of 8*32) the chunks turn per run: otherwise an XCD would take the
+  // same, lighter or heavier, slice of every head.
   p.xcd_group = 32;
   p.xcd_rotate = p.nb > 0 && (p.nb % (8 * p.xcd_group) == 0 || (8 * p.xcd_group) % p.nb == 0) ? 1 : 0;
 }
@@ -334,7 +333,6 @@ void fill_sparse(calibatt::AttnParams& p, const ListView* sl, int32_t t, int32_t
   p.row_ptr = sl->row_ptr;
   p.col_idx = sl->col_idx;
   p.runs = sl->runs;
-  p.order = sl->order;
   p.rec_head_rows = sl->nb;
   p.rec_row0 = ((int64_t)t * sl->L + l) * sl->H * sl->nb;
   p.n_sparse = (int32_t)heads.size();

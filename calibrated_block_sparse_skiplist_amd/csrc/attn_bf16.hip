@@ -79,7 +79,7 @@ __device__ __forceinline__ Item decode_item(const AttnParams& p, int64_t item) {
     it.anchor = false;
     it.head = p.sparse_heads[hi];
     const int64_t rec_row = p.rec_row0 + (int64_t)it.head * p.rec_head_rows;
-    it.tile = (p.order && p.use_order) ? p.order[rec_row + rank] : rank;
+    it.tile = rank;   // query blocks in block order: neighbours share key blocks in cache
     const int64_t b = p.row_ptr[rec_row + it.tile];
     const int64_t e = p.row_ptr[rec_row + it.tile + 1];
     it.list = p.runs ? nullptr : p.col_idx + b;

@@ -51,7 +51,7 @@ __global__ __launch_bounds__(BLK) void attn_f32_kernel(const AttnParams p) {
     head = p.sparse_heads[j / p.nb];
     const int rank = (int)(j % p.nb);
     const int64_t rec_row = p.rec_row0 + (int64_t)head * p.rec_head_rows;
-    tile = (p.order && p.use_order) ? p.order[rec_row + rank] : rank;
+    tile = rank;
     const int64_t b = p.row_ptr[rec_row + tile];
     list = p.runs ? nullptr : p.col_idx + b;
     runs = p.runs ? p.runs + b : nullptr;

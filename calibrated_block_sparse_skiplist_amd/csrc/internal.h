@@ -15,8 +15,8 @@ namespace calibatt {
 //     i % anchor_tiles of the gathered anchor queries (F*k*C of them, in
 //     (frame, anchor, column) order), visiting every key block;
 //   * block-sparse items follow: head sparse_heads[j / nb] visits the list of
-//     query block j % nb (or order[rec*nb + j % nb] when use_order is set and
-//     order is given; the entry points leave use_order at 0).
+//     query block j % nb (query blocks in block order: neighbours share most of
+//     their key blocks; the compiled heaviest-first order is not read).
 // Grid blocks map to items
 // XCD-aware: workgroups are dispatched round-robin over the 8 XCDs, so each
 // XCD's share of the grid is fixed in advance. Anchor items (all of one size)
@@ -39,13 +39,11 @@ struct AttnParams {
   // block-sparse items
   const int64_t* row_ptr;
   const int32_t* col_idx;
-  const int32_t* order;
   const uint32_t* runs;     // interval form: packed runs lo | hi << 16 (row_ptr then
                             // offsets runs, col_idx is unused); NULL for index lists
   int64_t rec_row0;         // skip-list row of (t, l, head 0, block 0)
   int32_t rec_head_rows;    // rows per record (= nb)
   int32_t n_sparse;
-  int32_t use_order;        // 1: visit query blocks heaviest-first; 0: in block order
   int32_t xcd_group;        // consecutive items given to one XCD (0: plain grid order)
   int32_t xcd_rotate;       // 1: the chunk of each XCD turns per run (runs that cover whole heads)
   // anchor items
