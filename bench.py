@@ -77,6 +77,10 @@ def parse_args():
                          "40 heads) resident on the GPU: compile both list forms, account memory, and stream "
                          "layer calls through sampled timesteps (one JSON line)")
     ap.add_argument("--run-steps", default="0,25,49", help="timesteps whose 40 layer calls are timed")
+    ap.add_argument("--profile", choices=["layer", "sweep"],
+                    help="a short fixed workload for rocprofv3 passes (no timing printed): 'layer' = the 720p "
+                         "skip-list compile x3, layer-call x3 (O only) and the same kernel dense over 8 heads x3; "
+                         "'sweep' = layer 0 of the 480p dictionary at sparsity 0, 0.68 and 0.85, x3 each")
     ap.add_argument("--no-extra-configs", action="store_true",
                     help="skip the 480p layers and the sweep summary in the default run")
     return ap.parse_args()
@@ -227,7 +231,9 @@ def cpu_baseline(wl, budget_s: float, flops_layer: float):
 
 
 def pmc_traffic(kernel_sha: str):
-    """HBM bytes per launch from the committed counter summary, if it matches this kernel source."""
+    """L2 <-> fabric bytes per launch (FETCH_SIZE + WRITE_SIZE, scaled by a 1 GiB copy; the MALL and HBM
+    together, an upper bound on HBM bytes) from the committed counter summary, if it matches this kernel
+    source."""
     path = os.path.join(ROOT, "profiles", "attn_wan720_hbm_counters.md")
     if not os.path.exists(path):
         return None
@@ -239,7 +245,7 @@ def pmc_traffic(kernel_sha: str):
     if vals.get("kernel_source_sha256", "")[:16] != kernel_sha[:16]:
         return None
     try:
-        return float(vals["hbm_bytes_per_launch"])
+        return float(vals["fabric_bytes_per_launch"])
     except (KeyError, ValueError):
         return None
 
@@ -628,6 +634,50 @@ def sweep_summary(layers: int = 2, reps: int = 5):
                         "(speedups against the 0 %-sparsity, 0 %-repetitive point)", "points": points}
 
 
+def profile_workload(kind: str):
+    """Fixed kernel sequences for counter passes (launches told apart by kernel name, grid and order)."""
+    import torch
+    import workloads
+    import calibrated_block_sparse_skiplist_amd as cal
+    dev = torch.device("cuda")
+    if kind == "layer":
+        wl = workloads.make_workload("wan720")
+        cfg = wl.cfg
+        q, k, v = (torch.from_numpy(x.view(np.int16)).view(torch.bfloat16).to(dev) for x in (wl.q, wl.k, wl.v))
+        o = torch.empty_like(q)
+        masks = torch.from_numpy(wl.masks).to(dev)
+        sl = cal.compile_skiplist(masks, cfg.N, cfg.B)
+        sld = cal.compile_skiplist(torch.ones((1, 1, cfg.H, cfg.nb, cfg.nb), dtype=torch.uint8, device=dev),
+                                   cfg.N, cfg.B)
+        torch.cuda.synchronize()
+        for _ in range(3):
+            cal.calibatt_compile_skiplist(masks, 1, 1, cfg.H, cfg.N, cfg.B, sl.row_ptr, sl.col_idx,
+                                          sl.col_idx.numel(), None)
+        for _ in range(3):
+            cal.calibatt_layer_dispatch(q, k, v, o, None, sl, 0, 0, wl.rep_flags, cfg.F, cfg.R, cfg.C, wl.anchors,
+                                        scale=wl.scale)
+        torch.cuda.synchronize()
+        for _ in range(3):
+            cal.calibatt_block_sparse_attn(q, k, v, o, None, sld, 0, 0, heads=list(range(8)), scale=wl.scale)
+    else:
+        base = workloads.get_config("wan480_dual")
+        q, k, v = workloads.make_qkv(base)
+        qd, kd, vd = (torch.from_numpy(x.view(np.int16)).view(torch.bfloat16).to(dev) for x in (q, k, v))
+        o = torch.empty_like(qd)
+        scale = float(np.float32(1.0 / np.sqrt(base.d)))
+        lists = []
+        for sp in (0.0, 0.68, 0.85):
+            cfg, masks, _ = workloads.make_dictionary_workload(sp, 0.0, L=1)
+            lists.append(cal.compile_skiplist(torch.from_numpy(masks).to(dev), cfg.N, cfg.B))
+        torch.cuda.synchronize()
+        for sl in lists:
+            for _ in range(3):
+                cal.calibatt_block_sparse_attn(qd, kd, vd, o, None, sl, 0, 0, scale=scale)
+            torch.cuda.synchronize()
+    torch.cuda.synchronize()
+    print(json.dumps({"profile": kind, "done": True}), flush=True)
+
+
 def main():
     args = parse_args()
     if args.gpus != 1:
@@ -636,6 +686,9 @@ def main():
               "of the heads)", file=sys.stderr)
         sys.exit(2)
     import torch
+    if args.profile:
+        profile_workload(args.profile)
+        return
     if args.dictionary_sweep:
         dictionary_sweep(args)
         return
@@ -867,7 +920,10 @@ def main():
                      "layer_interactions": work["layer_interaction_sparsity"]},
         "roofline": {"kernel": ATTN_KERNEL, "bound": "mfma", "achieved": round(achieved, 2),
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-                     "traffic": traffic, "flop_per_launch": flops, "launch_ms": round(attn_ms, 3)},
+                     "traffic": traffic,
+                     "traffic_kind": "L2<->fabric bytes per launch (MALL and HBM together; FETCH_SIZE + WRITE_SIZE "
+                                     "scaled by a 1 GiB copy)",
+                     "flop_per_launch": flops, "launch_ms": round(attn_ms, 3)},
         "cpu_baseline": cpu,
         "other_workloads": extra,
     }
