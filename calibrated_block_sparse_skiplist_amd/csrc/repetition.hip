@@ -62,7 +62,11 @@ __global__ __launch_bounds__(kMaxWaves * 64) void similarity_bf16_kernel(const S
   constexpr int RPI = 64 / CPR;          // K rows per copy
 
   __shared__ uint4 lds_k[2 * STAGE];
-  __shared__ float part[kMaxSlots][3];   // this pass's per-slot sums
+  // This pass's per-slot sums, 3 floats per slot, rows of the group one after
+  // the other; one pad float after each row when 3*C is even, so a row starts
+  // an odd number of words after the previous one and the rows' summing lanes
+  // (one per row, reading their rows in step) fall in distinct banks.
+  __shared__ float part[3 * kMaxSlots + kMaxSlots + 2];
   __shared__ float rowacc[kMaxSlots][3]; // per-row totals of the group
 
   const int lane = threadIdx.x & 63;
@@ -247,22 +251,38 @@ __global__ __launch_bounds__(kMaxWaves * 64) void similarity_bf16_kernel(const S
     dot = dot / (l_r * l_a);
     nr2 = nr2 / (l_r * l_r);
     na2 = na2 / (l_a * l_a);
-    if (h == 0) {
-      part[wave * 32 + l32][0] = dot;
-      part[wave * 32 + l32][1] = nr2;
-      part[wave * 32 + l32][2] = na2;
+    const int il0 = base / p.C;
+    const int pad = (3 * p.C) % 2 == 0 ? 1 : 0;   // words after each row of part[]
+    {
+      // One store per row among this wave's slots: a store whose lanes spanned
+      // two rows would put a padded lane in the bank of an unpadded one.
+      const int row = slot / p.C - il0;
+      const int first_slot = base + wave * 32;
+      const int r_lo = first_slot / p.C - il0;
+      const int r_hi = (first_slot + 31) / p.C - il0;
+      for (int rr = r_lo; rr <= r_hi; ++rr) {
+        if (h == 0 && row == rr) {
+          const int at = 3 * (slot - base) + pad * rr;
+          part[at + 0] = dot;
+          part[at + 1] = nr2;
+          part[at + 2] = na2;
+        }
+        __builtin_amdgcn_sched_barrier(0);   // (keep the rows' stores apart)
+      }
     }
     __syncthreads();
     // rows touched by this pass add their slots in column order
     const int end = min(base + W * 32, slots);
-    const int il0 = base / p.C, il1 = (end - 1) / p.C;
+    const int il1 = (end - 1) / p.C;
     for (int t = il0 + (int)threadIdx.x; t <= il1; t += blockDim.x) {
       const int s0 = max(t * p.C, base), s1 = min((t + 1) * p.C, end);
+      const int row_pad = pad * (t - il0);
       float sd = 0.0f, sn = 0.0f, sa2 = 0.0f;
       for (int q = s0; q < s1; ++q) {
-        sd += part[q - base][0];
-        sn += part[q - base][1];
-        sa2 += part[q - base][2];
+        const int at = 3 * (q - base) + row_pad;
+        sd += part[at + 0];
+        sn += part[at + 1];
+        sa2 += part[at + 2];
       }
       rowacc[t][0] += sd;
       rowacc[t][1] += sn;
