@@ -28,6 +28,11 @@ Citations name the web page and the section on it:
     intervals per query block ([Notes] Key Design 4; Highlights): one
     half-open [lo, hi) pair per maximal run of kept key blocks.
 
+``skiplist.compile_bitmap``
+    The same selection packed as one bit per key block (ceil(nb/64) 64-bit
+    words per query block, bit c % 64 of word c // 64), for dictionaries held
+    in the least memory.
+
 ``attention.block_sparse_head``
     Retained connections are computed from the current input's Q, K and V and
     unselected ones are skipped ([Notes] Overall Architecture; [Abstract]).
@@ -74,12 +79,13 @@ Readings of points the pages leave open are listed in the module docstrings
 where they are applied (empty rows, partial last block, anchor ties, token
 order, broadcast unit).
 """
-from .skiplist import compile_intervals, compile_skiplist, intervals_to_dense, skiplist_to_dense
+from .skiplist import (bitmap_to_dense, compile_bitmap, compile_intervals, compile_skiplist, intervals_to_dense,
+                       skiplist_to_dense)
 from .attention import (block_sparse_head, anchor_head, nearest_anchor_rows,
                         layer_forward, block_tokens)
 from .calibration import block_energy, keep_counts, keep_frequency_mask, select_blocks
 from .repetition import repetition_flags, repetition_mean, row_similarity
 
-__all__ = ["compile_intervals", "compile_skiplist", "intervals_to_dense", "skiplist_to_dense", "block_sparse_head", "anchor_head",
+__all__ = ["bitmap_to_dense", "compile_bitmap", "compile_intervals", "compile_skiplist", "intervals_to_dense", "skiplist_to_dense", "block_sparse_head", "anchor_head",
            "nearest_anchor_rows", "layer_forward", "block_tokens", "block_energy", "keep_counts",
            "keep_frequency_mask", "select_blocks", "repetition_flags", "repetition_mean", "row_similarity"]

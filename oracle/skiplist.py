@@ -17,6 +17,9 @@ Readings applied here (the pages leave them open):
   same set of blocks.)
 * order: for each record, the query blocks sorted by descending kept count,
   ties by ascending block index (heaviest first, for load balancing).
+* Bitmap form: the same selection as nb bits per row (bit c of the row set
+  iff key block c is kept), in W = ceil(nb/64) 64-bit words per row, key
+  block c in bit c % 64 of word c // 64; the bits past nb are zero.
 """
 from __future__ import annotations
 
@@ -111,4 +114,34 @@ def intervals_to_dense(iv_ptr: np.ndarray, iv: np.ndarray, T: int, L: int, H: in
     for row in range(T * L * H * nb):
         for lo, hi in iv[iv_ptr[row]:iv_ptr[row + 1]]:
             out[row, lo:hi] = 1
+    return out.reshape(T, L, H, nb, nb)
+
+
+def compile_bitmap(masks: np.ndarray) -> np.ndarray:
+    """Bitmap form of the skip list: uint64 [rows, W], W = ceil(nb / 64).
+
+    The selection of each row ([Notes] Key Design 4: per query block, the key
+    blocks to compute) as one bit per key block: bit (c % 64) of word (c // 64)
+    is 1 exactly when mask[row][c] != 0; bits at positions >= nb stay 0. Rows
+    are flattened as in compile_skiplist. Written from that definition: start
+    from all-zero words and set the bit of every kept block, column by column.
+    """
+    masks = np.asarray(masks)
+    if masks.ndim != 5 or masks.shape[3] != masks.shape[4]:
+        raise ValueError("masks must be [T, L, H, nb, nb]")
+    T, L, H, nb, _ = masks.shape
+    rows = masks.reshape(T * L * H * nb, nb) != 0
+    words = (nb + 63) // 64
+    bits = np.zeros((rows.shape[0], words), dtype=np.uint64)
+    for c in range(nb):
+        bits[:, c // 64] |= rows[:, c].astype(np.uint64) << np.uint64(c % 64)
+    return bits
+
+
+def bitmap_to_dense(bits: np.ndarray, T: int, L: int, H: int, nb: int) -> np.ndarray:
+    """Inverse of the bitmap encoding: rebuild the uint8 [T, L, H, nb, nb] keep mask."""
+    bits = np.asarray(bits, dtype=np.uint64)
+    out = np.zeros((T * L * H * nb, nb), dtype=np.uint8)
+    for c in range(nb):
+        out[:, c] = ((bits[:, c // 64] >> np.uint64(c % 64)) & np.uint64(1)).astype(np.uint8)
     return out.reshape(T, L, H, nb, nb)
