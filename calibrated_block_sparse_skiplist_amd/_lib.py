@@ -30,6 +30,8 @@ EXPORTED = (
     "calibatt_last_error", "calibatt_set_kernel_events", "calibatt_version",
     "calibatt_validate_skiplist", "calibatt_validate_intervals", "calibatt_set_checked_mode",
     "calibatt_block_energy_noalloc",
+    "calibatt_compile_bitmap", "calibatt_block_sparse_attn_bm", "calibatt_layer_dispatch_bm",
+    "calibatt_validate_bitmap",
 )
 NOALLOC_SCRATCH_BYTES = 256 << 20
 
@@ -52,6 +54,13 @@ class IntervalListView(ctypes.Structure):
     _fields_ = [("T", ctypes.c_int32), ("L", ctypes.c_int32), ("H", ctypes.c_int32),
                 ("N", ctypes.c_int32), ("B", ctypes.c_int32), ("nb", ctypes.c_int32),
                 ("iv_ptr", ctypes.c_void_p), ("iv", ctypes.c_void_p), ("order", ctypes.c_void_p)]
+
+
+class BitmapView(ctypes.Structure):
+    """Mirror of calibatt_bitmap_t."""
+    _fields_ = [("T", ctypes.c_int32), ("L", ctypes.c_int32), ("H", ctypes.c_int32),
+                ("N", ctypes.c_int32), ("B", ctypes.c_int32), ("nb", ctypes.c_int32), ("words", ctypes.c_int32),
+                ("bits", ctypes.c_void_p)]
 
 
 def _load():
@@ -111,6 +120,17 @@ def _load():
     lib.calibatt_set_checked_mode.restype = None
     lib.calibatt_block_energy_noalloc.argtypes = [vp, vp, i32, i32, i32, i32, f32, i32, vp, vp, i32, vp]
     lib.calibatt_block_energy_noalloc.restype = i32
+    lib.calibatt_compile_bitmap.argtypes = [vp, i32, i32, i32, i32, i32, vp, vp]
+    lib.calibatt_compile_bitmap.restype = i32
+    lib.calibatt_block_sparse_attn_bm.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, f32,
+                                                  ctypes.POINTER(BitmapView), i32, i32, vp, i32, vp]
+    lib.calibatt_block_sparse_attn_bm.restype = i32
+    lib.calibatt_layer_dispatch_bm.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, f32,
+                                               ctypes.POINTER(BitmapView), i32, i32, vp,
+                                               i32, i32, i32, vp, i32, vp]
+    lib.calibatt_layer_dispatch_bm.restype = i32
+    lib.calibatt_validate_bitmap.argtypes = [ctypes.POINTER(BitmapView), i32, i32, i32, vp]
+    lib.calibatt_validate_bitmap.restype = i32
     return lib
 
 
@@ -253,6 +273,71 @@ def compile_intervals(masks, N: int, B: int, with_order: bool = True, stream=Non
     order = torch.empty(rows, dtype=torch.int32, device=dev) if with_order else None
     calibatt_compile_intervals(masks, T, L, H, N, B, iv_ptr, iv, iv.numel(), order, stream)
     return IntervalList(T, L, H, N, B, nb, iv_ptr, iv, order, n_iv)
+
+
+@dataclass
+class Bitmap:
+    """A compiled dictionary in bitmap form held in a device tensor (bits: int64 storage of the uint64 words)."""
+    T: int
+    L: int
+    H: int
+    N: int
+    B: int
+    nb: int
+    words: int
+    bits: object
+
+    def view(self) -> BitmapView:
+        return BitmapView(self.T, self.L, self.H, self.N, self.B, self.nb, self.words, _ptr(self.bits))
+
+
+def calibatt_compile_bitmap(masks, T, L, H, N, B, bits, stream=None) -> None:
+    """Raw call: device masks in, bits (device tensor of T*L*H*nb*ceil(nb/64) 64-bit words) written."""
+    _check(lib.calibatt_compile_bitmap(_ptr(masks), T, L, H, N, B, _ptr(bits), _stream(stream)))
+
+
+def compile_bitmap(masks, N: int, B: int, stream=None) -> Bitmap:
+    """Compile uint8 device masks [T, L, H, nb, nb] into a Bitmap (allocates with torch)."""
+    import torch
+    T, L, H, nb, nb2 = masks.shape
+    if nb != nb2 or nb != -(-N // B):
+        raise ValueError("masks must be [T, L, H, nb, nb] with nb = ceil(N/B)")
+    words = -(-nb // 64)
+    bits = torch.empty((T * L * H * nb, words), dtype=torch.int64, device=masks.device)
+    calibatt_compile_bitmap(masks, T, L, H, N, B, bits, stream)
+    return Bitmap(T, L, H, N, B, nb, words, bits)
+
+
+def calibatt_block_sparse_attn_bm(q, k, v, o, lse, bm: Bitmap, t: int, l: int, heads=None,
+                                  scale: float | None = None, stream=None) -> None:
+    H, N, d = q.shape
+    scale = float(np.float32(1.0 / np.sqrt(d))) if scale is None else scale
+    harr, nh = _host_i32(heads)
+    view = bm.view()
+    _check(lib.calibatt_block_sparse_attn_bm(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), H, N, d,
+                                             _dtype_code(q), scale, ctypes.byref(view), t, l,
+                                             harr.ctypes.data if harr is not None else None, nh,
+                                             _stream(stream)))
+
+
+def calibatt_layer_dispatch_bm(q, k, v, o, lse, bm: Bitmap, t: int, l: int, rep_flags, F: int, R: int,
+                               C: int, anchor_rows, scale: float | None = None, stream=None) -> None:
+    H, N, d = q.shape
+    scale = float(np.float32(1.0 / np.sqrt(d))) if scale is None else scale
+    flags = np.ascontiguousarray(np.asarray(rep_flags, dtype=np.uint8))
+    if flags.shape != (bm.T, bm.L, bm.H):
+        raise ValueError("rep_flags must be [T, L, H] of the dictionary")
+    aarr, ka = _host_i32(anchor_rows)
+    view = bm.view()
+    _check(lib.calibatt_layer_dispatch_bm(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), H, N, d,
+                                          _dtype_code(q), scale, ctypes.byref(view), t, l,
+                                          flags.ctypes.data, F, R, C, aarr.ctypes.data, ka, _stream(stream)))
+
+
+def calibatt_validate_bitmap(bm: Bitmap, t: int = -1, l: int = -1, stream=None) -> None:
+    """Checked mode for a Bitmap (device tensor)."""
+    view = bm.view()
+    _check(lib.calibatt_validate_bitmap(ctypes.byref(view), t, l, 0, _stream(stream)))
 
 
 def calibatt_block_sparse_attn(q, k, v, o, lse, sl: SkipList, t: int, l: int, heads=None,

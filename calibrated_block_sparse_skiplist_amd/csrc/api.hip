@@ -84,27 +84,38 @@ calibatt_status_t check_heads(const int32_t* heads, int32_t n_heads, int32_t H, 
   return CALIBATT_OK;
 }
 
-// Either form of a compiled dictionary: index lists (row_ptr, col_idx) or runs
-// (row_ptr = iv_ptr, runs = iv).
+// Any form of a compiled dictionary: index lists (row_ptr, col_idx), runs
+// (row_ptr = iv_ptr, runs = iv) or bitmaps (bits, `words` per row).
 struct ListView {
   int32_t T, L, H, N, B, nb;
   const int64_t* row_ptr;
   const int32_t* col_idx;
   const uint32_t* runs;
   const int32_t* order;
+  const uint64_t* bits;
+  int32_t words;
 };
 
 calibatt_status_t view_of(const calibatt_skiplist_t* sl, ListView* v) {
   if (!sl) return fail(CALIBATT_ERR_INVALID_ARG, "skip list view is NULL");
   if (!sl->row_ptr || !sl->col_idx) return fail(CALIBATT_ERR_INVALID_ARG, "skip list row_ptr/col_idx are NULL");
-  *v = {sl->T, sl->L, sl->H, sl->N, sl->B, sl->nb, sl->row_ptr, sl->col_idx, nullptr, sl->order};
+  *v = {sl->T, sl->L, sl->H, sl->N, sl->B, sl->nb, sl->row_ptr, sl->col_idx, nullptr, sl->order, nullptr, 0};
   return CALIBATT_OK;
 }
 
 calibatt_status_t view_of(const calibatt_intervals_t* il, ListView* v) {
   if (!il) return fail(CALIBATT_ERR_INVALID_ARG, "interval list view is NULL");
   if (!il->iv_ptr || !il->iv) return fail(CALIBATT_ERR_INVALID_ARG, "interval list iv_ptr/iv are NULL");
-  *v = {il->T, il->L, il->H, il->N, il->B, il->nb, il->iv_ptr, nullptr, il->iv, il->order};
+  *v = {il->T, il->L, il->H, il->N, il->B, il->nb, il->iv_ptr, nullptr, il->iv, il->order, nullptr, 0};
+  return CALIBATT_OK;
+}
+
+calibatt_status_t view_of(const calibatt_bitmap_t* bm, ListView* v) {
+  if (!bm) return fail(CALIBATT_ERR_INVALID_ARG, "bitmap view is NULL");
+  if (!bm->bits) return fail(CALIBATT_ERR_INVALID_ARG, "bitmap bits are NULL");
+  if (bm->nb < 1 || bm->words != ceil_div(bm->nb, 64))
+    return fail(CALIBATT_ERR_INVALID_ARG, "bitmap words (%d) != ceil(nb/64) with nb = %d", bm->words, bm->nb);
+  *v = {bm->T, bm->L, bm->H, bm->N, bm->B, bm->nb, nullptr, nullptr, nullptr, nullptr, bm->bits, bm->words};
   return CALIBATT_OK;
 }
 
@@ -198,6 +209,25 @@ calibatt_status_t validate_view(const ListView* v, int32_t t, int32_t l, bool ho
   const int64_t rec0 = whole ? 0 : ((int64_t)t * v->L + l) * v->H;
   const int64_t recs = whole ? (int64_t)v->T * v->L * v->H : v->H;
   const int64_t row0 = rec0 * v->nb, rows = recs * v->nb;
+  if (v->bits) {
+    // bitmaps: the only constraint is that the bits past nb are zero
+    const uint64_t* words = v->bits + row0 * v->words;
+    std::vector<uint64_t> hw;
+    if (!host_arrays) {
+      hw.resize(rows * v->words);
+      hipError_t e = hipMemcpyAsync(hw.data(), words, hw.size() * sizeof(uint64_t), hipMemcpyDeviceToHost, s);
+      if (e == hipSuccess) e = hipStreamSynchronize(s);
+      if (e != hipSuccess) return hip_fail(e, "reading the bitmaps");
+      words = hw.data();
+    }
+    if (v->nb % 64) {
+      const uint64_t pad = ~((1ull << (v->nb % 64)) - 1ull);
+      for (int64_t i = 0; i < rows; ++i)
+        if (words[i * v->words + v->words - 1] & pad)
+          return fail(CALIBATT_ERR_INVALID_ARG, "row %lld: bits set past nb = %d", (long long)(row0 + i), v->nb);
+    }
+    return CALIBATT_OK;
+  }
   std::vector<int64_t> hp;
   std::vector<int32_t> hi;
   std::vector<uint32_t> hr;
@@ -333,6 +363,8 @@ void fill_sparse(calibatt::AttnParams& p, const ListView* sl, int32_t t, int32_t
   p.row_ptr = sl->row_ptr;
   p.col_idx = sl->col_idx;
   p.runs = sl->runs;
+  p.bits = sl->bits;
+  p.bm_words = sl->words;
   p.rec_head_rows = sl->nb;
   p.rec_row0 = ((int64_t)t * sl->L + l) * sl->H * sl->nb;
   p.n_sparse = (int32_t)heads.size();
@@ -505,6 +537,29 @@ calibatt_status_t calibatt_validate_intervals(const calibatt_intervals_t* il, in
   return ok();
 }
 
+calibatt_status_t calibatt_validate_bitmap(const calibatt_bitmap_t* bm, int32_t t, int32_t l, int32_t host_arrays,
+                                           void* stream) {
+  ListView view;
+  calibatt_status_t st = view_of(bm, &view);
+  if (st != CALIBATT_OK) return st;
+  if ((st = validate_view(&view, t, l, host_arrays != 0, static_cast<hipStream_t>(stream))) != CALIBATT_OK) return st;
+  return ok();
+}
+
+calibatt_status_t calibatt_compile_bitmap(const uint8_t* masks, int32_t T, int32_t L, int32_t H, int32_t N, int32_t B,
+                                          uint64_t* bits, void* stream) {
+  if (!masks || !bits) return fail(CALIBATT_ERR_INVALID_ARG, "masks and bits must be non-NULL");
+  if (T < 1 || L < 1 || H < 1 || N < 1 || B < 1)
+    return fail(CALIBATT_ERR_INVALID_ARG, "T, L, H, N and B must be >= 1");
+  const int64_t nb = ceil_div(N, B);
+  if (nb > CALIBATT_MAX_NB) return fail(CALIBATT_ERR_INVALID_ARG, "nb = %lld exceeds %d", (long long)nb, CALIBATT_MAX_NB);
+  if (reinterpret_cast<uintptr_t>(bits) % 8 != 0) return fail(CALIBATT_ERR_INVALID_ARG, "bits is not 8-byte aligned");
+  const int64_t rows = (int64_t)T * L * H * nb;
+  hipError_t e = calibatt::launch_compile_bitmap(masks, rows, (int)nb, bits, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "bitmap kernel launch");
+  return ok();
+}
+
 calibatt_status_t calibatt_compile_skiplist(const uint8_t* masks, int32_t T, int32_t L, int32_t H, int32_t N,
                                             int32_t B, int64_t* row_ptr, int32_t* col_idx, int64_t col_capacity,
                                             int32_t* order, int64_t* nnz_out, void* stream) {
@@ -536,6 +591,17 @@ calibatt_status_t calibatt_block_sparse_attn_iv(const void* q, const void* k, co
   if (st != CALIBATT_OK) return st;
   ListView view;
   if ((st = view_of(il, &view)) != CALIBATT_OK) return st;
+  return sparse_impl(q, k, v, o, lse, H, N, d, dtype, scale, &view, t, l, heads, n_heads, stream);
+}
+
+calibatt_status_t calibatt_block_sparse_attn_bm(const void* q, const void* k, const void* v, void* o, float* lse,
+                                                int32_t H, int32_t N, int32_t d, calibatt_dtype_t dtype,
+                                                float scale, const calibatt_bitmap_t* bm, int32_t t, int32_t l,
+                                                const int32_t* heads, int32_t n_heads, void* stream) {
+  calibatt_status_t st = check_tensors(q, k, v, o, H, N, d, dtype, scale);
+  if (st != CALIBATT_OK) return st;
+  ListView view;
+  if ((st = view_of(bm, &view)) != CALIBATT_OK) return st;
   return sparse_impl(q, k, v, o, lse, H, N, d, dtype, scale, &view, t, l, heads, n_heads, stream);
 }
 
@@ -581,6 +647,19 @@ calibatt_status_t calibatt_layer_dispatch_iv(const void* q, const void* k, const
   if (st != CALIBATT_OK) return st;
   ListView view;
   if ((st = view_of(il, &view)) != CALIBATT_OK) return st;
+  return dispatch_impl(q, k, v, o, lse, H, N, d, dtype, scale, &view, t, l, rep_flags, F, R, C, anchor_rows,
+                       k_anchors, stream);
+}
+
+calibatt_status_t calibatt_layer_dispatch_bm(const void* q, const void* k, const void* v, void* o, float* lse,
+                                             int32_t H, int32_t N, int32_t d, calibatt_dtype_t dtype, float scale,
+                                             const calibatt_bitmap_t* bm, int32_t t, int32_t l,
+                                             const uint8_t* rep_flags, int32_t F, int32_t R, int32_t C,
+                                             const int32_t* anchor_rows, int32_t k_anchors, void* stream) {
+  calibatt_status_t st = check_tensors(q, k, v, o, H, N, d, dtype, scale);
+  if (st != CALIBATT_OK) return st;
+  ListView view;
+  if ((st = view_of(bm, &view)) != CALIBATT_OK) return st;
   return dispatch_impl(q, k, v, o, lse, H, N, d, dtype, scale, &view, t, l, rep_flags, F, R, C, anchor_rows,
                        k_anchors, stream);
 }

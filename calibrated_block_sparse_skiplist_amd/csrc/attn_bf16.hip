@@ -59,7 +59,9 @@ struct Item {
   int tile;              // query block (sparse) or anchor tile
   const int32_t* list;   // index-list form: the key blocks
   const uint32_t* runs;  // interval form: packed runs lo | hi << 16
-  int n;                 // key blocks to visit (index list, anchor), or runs (interval form)
+  const uint64_t* bits;  // bitmap form: the row's words (expanded to an index list in LDS)
+  int n;                 // key blocks to visit (index list, anchor), or runs (interval form);
+                         // bitmap form: counted from the words
 };
 
 __device__ __forceinline__ Item decode_item(const AttnParams& p, int64_t item) {
@@ -71,6 +73,7 @@ __device__ __forceinline__ Item decode_item(const AttnParams& p, int64_t item) {
     it.tile = (int)(item % p.anchor_tiles);
     it.list = nullptr;
     it.runs = nullptr;
+    it.bits = nullptr;
     it.n = p.nb;
   } else {
     const int64_t j = item - n_anchor_items;
@@ -80,11 +83,19 @@ __device__ __forceinline__ Item decode_item(const AttnParams& p, int64_t item) {
     it.head = p.sparse_heads[hi];
     const int64_t rec_row = p.rec_row0 + (int64_t)it.head * p.rec_head_rows;
     it.tile = rank;   // query blocks in block order: neighbours share key blocks in cache
-    const int64_t b = p.row_ptr[rec_row + it.tile];
-    const int64_t e = p.row_ptr[rec_row + it.tile + 1];
-    it.list = p.runs ? nullptr : p.col_idx + b;
-    it.runs = p.runs ? p.runs + b : nullptr;
-    it.n = (int)(e - b);
+    if (p.bits) {
+      it.list = nullptr;
+      it.runs = nullptr;
+      it.bits = p.bits + (rec_row + it.tile) * p.bm_words;
+      it.n = 0;
+    } else {
+      const int64_t b = p.row_ptr[rec_row + it.tile];
+      const int64_t e = p.row_ptr[rec_row + it.tile + 1];
+      it.list = p.runs ? nullptr : p.col_idx + b;
+      it.runs = p.runs ? p.runs + b : nullptr;
+      it.bits = nullptr;
+      it.n = (int)(e - b);
+    }
   }
   return it;
 }
@@ -159,11 +170,37 @@ void attn_bf16_kernel(const AttnParams p) {
   // once (nb <= CALIBATT_MAX_NB, as the host checks), so the loop reads
   // indices with LDS broadcasts instead of vector-memory loads, which would
   // join the vmcnt queue of the prefetch.
+  // A bitmap row is expanded into the same index list: lane w of every wave
+  // takes word w (bm_words <= 64) and the set bits are counted with a wave
+  // prefix sum; wave 0 writes each lane's blocks, ascending, after those of
+  // the lanes before it.
+  int n_listed = it.n;
   if (it.list) {
     for (int i = threadIdx.x; i < it.n; i += NW * 64) lds_list[i] = (uint16_t)it.list[i];
   } else if (it.runs) {
     for (int i = threadIdx.x; i < it.n; i += NW * 64) lds_list32[i] = it.runs[i];
+  } else if (it.bits) {
+    uint64_t word = lane < p.bm_words ? it.bits[lane] : 0ull;
+    // (bits past nb are zero in a compiled bitmap; they are dropped anyway, so
+    // no listed block ever lies past the sequence)
+    if (lane == p.bm_words - 1 && (p.nb & 63)) word &= (1ull << (p.nb & 63)) - 1ull;
+    const int cnt = __popcll(word);
+    int incl = cnt;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const int y = __shfl_up(incl, off);
+      if (lane >= off) incl += y;
+    }
+    n_listed = __builtin_amdgcn_readlane(incl, 63);
+    if (wave == 0) {
+      int pos = incl - cnt;
+      while (word) {
+        lds_list[pos++] = (uint16_t)(64 * lane + __builtin_ctzll(word));
+        word &= word - 1;
+      }
+    }
   }
+  const bool idx_list = it.list || it.bits;   // key blocks staged as an index list
 
   // Q^T operand fragments: query = wave*32 + l32, d = 16*s + 8*h + [0, 8).
   const int qtok = query_token(p, it, wave * 32 + l32, BLK);
@@ -229,7 +266,7 @@ void attn_bf16_kernel(const AttnParams p) {
       run_hi = (int)(w >> 16);
       return (int)(w & 0xffffu);
     }
-    return it.list ? __builtin_amdgcn_readfirstlane((int)lds_list[0]) : 0;
+    return idx_list ? __builtin_amdgcn_readfirstlane((int)lds_list[0]) : 0;
   };
   auto next_block = [&](int c, int i) -> int {   // i: step of the block that follows c
     if (it.runs) {
@@ -238,7 +275,7 @@ void attn_bf16_kernel(const AttnParams p) {
       run_hi = (int)(w >> 16);
       return (int)(w & 0xffffu);
     }
-    return it.list ? __builtin_amdgcn_readfirstlane((int)lds_list[i]) : i;
+    return idx_list ? __builtin_amdgcn_readfirstlane((int)lds_list[i]) : i;
   };
 
   f32x16 oacc[DT];
@@ -265,7 +302,7 @@ void attn_bf16_kernel(const AttnParams p) {
 
   // Blocks to visit: the run lengths summed (every wave sums the staged runs
   // itself, so no extra barrier), or the list length.
-  int n_blocks = it.n;
+  int n_blocks = n_listed;
   if (it.runs) {
     int part = 0;
     for (int i = lane; i < it.n; i += 64) {

@@ -39,6 +39,7 @@ __global__ __launch_bounds__(BLK) void attn_f32_kernel(const AttnParams p) {
   int head, tile, n;
   const int32_t* list;
   const uint32_t* runs = nullptr;
+  const uint64_t* bits = nullptr;
   if (item < n_anchor_items) {
     anchor = true;
     head = p.anchor_heads[item / p.anchor_tiles];
@@ -52,10 +53,17 @@ __global__ __launch_bounds__(BLK) void attn_f32_kernel(const AttnParams p) {
     const int rank = (int)(j % p.nb);
     const int64_t rec_row = p.rec_row0 + (int64_t)head * p.rec_head_rows;
     tile = rank;
-    const int64_t b = p.row_ptr[rec_row + tile];
-    list = p.runs ? nullptr : p.col_idx + b;
-    runs = p.runs ? p.runs + b : nullptr;
-    n = (int)(p.row_ptr[rec_row + tile + 1] - b);
+    if (p.bits) {
+      // bitmap form: visit the set bits word by word (n counts words)
+      bits = p.bits + (rec_row + tile) * p.bm_words;
+      list = nullptr;
+      n = p.bm_words;
+    } else {
+      const int64_t b = p.row_ptr[rec_row + tile];
+      list = p.runs ? nullptr : p.col_idx + b;
+      runs = p.runs ? p.runs + b : nullptr;
+      n = (int)(p.row_ptr[rec_row + tile + 1] - b);
+    }
   }
 
   const float* Q = static_cast<const float*>(p.q) + (int64_t)head * p.head_stride;
@@ -72,12 +80,23 @@ __global__ __launch_bounds__(BLK) void attn_f32_kernel(const AttnParams p) {
   float m = -INFINITY, l = 0.0f;
 
   // Visit key blocks run by run: a run of the interval form, or one block of
-  // an index list (anchor items: every block).
+  // an index list (anchor items: every block); bitmap form: the set bits of
+  // each word, ascending (bits past nb dropped).
   for (int step = 0; step < n; ++step) {
     const uint32_t w = runs ? runs[step] : 0u;
+    uint64_t word = 0;
+    if (bits) {
+      word = bits[step];
+      if (step == p.bm_words - 1 && (p.nb & 63)) word &= (1ull << (p.nb & 63)) - 1ull;
+    }
     const int lo = runs ? (int)(w & 0xffffu) : (list ? list[step] : step);
     const int hi = runs ? (int)(w >> 16) : lo + 1;
-    for (int c = lo; c < hi; ++c) {
+    for (int c0 = bits ? 64 * step : lo; bits ? word != 0 : c0 < hi; ++c0) {
+      int c = c0;
+      if (bits) {
+        c = 64 * step + __builtin_ctzll(word);
+        word &= word - 1;
+      }
       const int nk = min(BLK, p.N - c * BLK);
       __syncthreads();
       for (int e = threadIdx.x * 4; e < nk * D; e += BLK * 4) {

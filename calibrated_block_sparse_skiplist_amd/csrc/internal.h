@@ -41,6 +41,9 @@ struct AttnParams {
   const int32_t* col_idx;
   const uint32_t* runs;     // interval form: packed runs lo | hi << 16 (row_ptr then
                             // offsets runs, col_idx is unused); NULL for index lists
+  const uint64_t* bits;     // bitmap form: bm_words words per row (row_ptr, col_idx and
+                            // runs unused); NULL otherwise
+  int32_t bm_words;         // ceil(nb / 64)
   int64_t rec_row0;         // skip-list row of (t, l, head 0, block 0)
   int32_t rec_head_rows;    // rows per record (= nb)
   int32_t n_sparse;
@@ -139,5 +142,6 @@ hipError_t launch_compile_runs_count_scan(const uint8_t* masks, int64_t rows, in
 hipError_t launch_compile_runs_fill(const uint8_t* masks, int64_t rows, int nb, const int64_t* iv_ptr,
                                     uint32_t* iv, int32_t* kept_out, hipStream_t s);
 hipError_t launch_compile_runs_order(int64_t records, int nb, int32_t* order, hipStream_t s);
+hipError_t launch_compile_bitmap(const uint8_t* masks, int64_t rows, int nb, uint64_t* bits, hipStream_t s);
 
 }  // namespace calibatt

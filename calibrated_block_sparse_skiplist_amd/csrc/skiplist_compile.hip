@@ -412,6 +412,28 @@ hipError_t scan_counts(int64_t rows, int64_t* row_ptr, hipStream_t s) {
   return e;
 }
 
+// Bitmap form: row r's key block c is bit c % 64 of word c / 64 of the row's
+// `words` words. One wave per row (waves stride over rows): word w is the
+// ballot of "byte 64w + lane of the row is nonzero" over the wave's lanes, so
+// one coalesced 64-byte load gives one word; lane w keeps word w and the
+// row's words are stored together. Columns past nb read nothing and stay 0.
+__global__ __launch_bounds__(kThreads) void bitmap_kernel(const uint8_t* __restrict__ masks, int64_t rows, int nb,
+                                                          int words, uint64_t* __restrict__ bits) {
+  const int lane = threadIdx.x & 63;
+  const int64_t stride = (int64_t)gridDim.x * kWaves;
+  for (int64_t r = (int64_t)blockIdx.x * kWaves + (threadIdx.x >> 6); r < rows; r += stride) {
+    const uint8_t* row = masks + r * nb;
+    uint64_t mine = 0;
+    for (int w = 0; w < words; ++w) {
+      const int c = 64 * w + lane;
+      const bool keep = c < nb && row[c] != 0;
+      const uint64_t word = __ballot(keep);
+      if (lane == w) mine = word;
+    }
+    if (lane < words) bits[r * words + lane] = mine;
+  }
+}
+
 }  // namespace
 
 // Workgroups of the row-striding kernels: enough waves to keep every CU's
@@ -428,6 +450,14 @@ hipError_t launch_compile_count_scan(const uint8_t* masks, int64_t rows, int nb,
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   return scan_counts(rows, row_ptr, s);
+}
+
+hipError_t launch_compile_bitmap(const uint8_t* masks, int64_t rows, int nb, uint64_t* bits, hipStream_t s) {
+  if (rows == 0) return hipSuccess;
+  const int words = (nb + 63) / 64;
+  if (words > 64) return hipErrorInvalidValue;   // (nb <= CALIBATT_MAX_NB: at most 64 words, one per lane)
+  hipLaunchKernelGGL(bitmap_kernel, dim3(stride_grid(rows)), dim3(kThreads), 0, s, masks, rows, nb, words, bits);
+  return hipGetLastError();
 }
 
 hipError_t launch_compile_fill(const uint8_t* masks, int64_t rows, int nb, const int64_t* row_ptr,

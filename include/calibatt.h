@@ -228,6 +228,58 @@ calibatt_status_t calibatt_layer_dispatch_iv(const void* q, const void* k, const
                                              const int32_t* anchor_rows, int32_t k_anchors, void* stream);
 
 /*
+ * The bitmap form of a compiled dictionary: the same selection as the lists,
+ * one bit per key block ([Notes] Key Design 4: per query block, the key blocks
+ * to compute), for dictionaries held in the least memory ([Notes] Limitations:
+ * the masks of a whole Wan-720p run take tens of GB in the pages' own form).
+ * Row r = ((t*L + l)*H + h)*nb + q of record (t, l, h), query block q, holds
+ * `words` = ceil(nb/64) uint64 words; key block c is bit (c % 64) of word
+ * (c / 64) (value 2^(c % 64)); bits past nb are zero. Fixed size per record:
+ * no row pointers, and its compile needs no count read-back. A view of
+ * caller-owned device memory, as produced by calibatt_compile_bitmap.
+ *   T, L, H, N, B, nb: as in calibatt_skiplist_t.
+ *   words : ceil(nb / 64).
+ *   bits  : uint64 [T*L*H*nb][words].
+ */
+typedef struct {
+  int32_t T, L, H, N, B, nb, words;
+  const uint64_t* bits;
+} calibatt_bitmap_t;
+
+/*
+ * Compile binary block masks into the bitmap form (same masks, T, L, H, N, B
+ * rules as calibatt_compile_skiplist).
+ *   bits   uint64 [T*L*H*nb][ceil(nb/64)], device, 8-byte aligned, written.
+ * Asynchronous: the size is known in advance, so nothing is read back.
+ */
+calibatt_status_t calibatt_compile_bitmap(const uint8_t* masks, int32_t T, int32_t L, int32_t H, int32_t N,
+                                          int32_t B, uint64_t* bits, void* stream);
+
+/*
+ * calibatt_block_sparse_attn over a dictionary in bitmap form: each query
+ * block's set bits are expanded, ascending, into the kernels' key-block list,
+ * so the blocks, their order and the arithmetic are those of the index-list
+ * form and the outputs are bitwise equal to calibatt_block_sparse_attn's.
+ * Bits past nb are ignored. Same arguments and rules, with `bm` in place of `sl`.
+ */
+calibatt_status_t calibatt_block_sparse_attn_bm(const void* q, const void* k, const void* v, void* o,
+                                                float* lse, int32_t H, int32_t N, int32_t d,
+                                                calibatt_dtype_t dtype, float scale,
+                                                const calibatt_bitmap_t* bm, int32_t t, int32_t l,
+                                                const int32_t* heads, int32_t n_heads, void* stream);
+
+/*
+ * calibatt_layer_dispatch over a dictionary in bitmap form (rep_flags is
+ * [T][L][H] with T, L, H taken from *bm). Bitwise equal to the index-list call.
+ */
+calibatt_status_t calibatt_layer_dispatch_bm(const void* q, const void* k, const void* v, void* o,
+                                             float* lse, int32_t H, int32_t N, int32_t d,
+                                             calibatt_dtype_t dtype, float scale,
+                                             const calibatt_bitmap_t* bm, int32_t t, int32_t l,
+                                             const uint8_t* rep_flags, int32_t F, int32_t R, int32_t C,
+                                             const int32_t* anchor_rows, int32_t k_anchors, void* stream);
+
+/*
  * ---- Checked mode (for list views the caller built or loaded itself) ----
  *
  * The attention calls trust a view's contents: the compile calls produce
@@ -253,10 +305,13 @@ calibatt_status_t calibatt_validate_skiplist(const calibatt_skiplist_t* sl, int3
                                              int32_t host_arrays, void* stream);
 calibatt_status_t calibatt_validate_intervals(const calibatt_intervals_t* il, int32_t t, int32_t l,
                                               int32_t host_arrays, void* stream);
+/* Bitmaps: words == ceil(nb/64), and the bits past nb are zero. */
+calibatt_status_t calibatt_validate_bitmap(const calibatt_bitmap_t* bm, int32_t t, int32_t l,
+                                           int32_t host_arrays, void* stream);
 
 /*
- * Checked mode for this thread: when enabled, calibatt_block_sparse_attn(_iv)
- * and calibatt_layer_dispatch(_iv) validate the record (t, l) they are given,
+ * Checked mode for this thread: when enabled, calibatt_block_sparse_attn(_iv,
+ * _bm) and calibatt_layer_dispatch(_iv, _bm) validate the record (t, l) they are given,
  * as calibatt_validate_* does (copying its lists to host memory and
  * synchronising `stream`), before anything is enqueued; a malformed record
  * returns CALIBATT_ERR_INVALID_ARG and no kernel runs. Off by default (the

@@ -371,3 +371,42 @@ def test_checked_mode_switch():
     # the switch is thread-local state; toggling it makes no HIP call
     lib.calibatt_set_checked_mode(1)
     lib.calibatt_set_checked_mode(0)
+
+
+def _validate_bm(T, L, H, N, B, bits, words=None, t=-1, l=-1):
+    nb = -(-N // B)
+    w = -(-nb // 64) if words is None else words
+    view = cal.BitmapView(T, L, H, N, B, nb, w, bits.ctypes.data)
+    return lib.calibatt_validate_bitmap(ctypes.byref(view), t, l, 1, None)
+
+
+def test_validate_bitmaps():
+    import oracle
+    rng = np.random.default_rng(5)
+    for N, B in ((1000, 128), (640 * 64, 64), (129, 1)):
+        nb = -(-N // B)
+        if nb > cal.MAX_NB:
+            continue
+        masks = (rng.random((1, 2, 2, nb, nb)) < 0.3).astype(np.uint8)
+        bits = np.ascontiguousarray(oracle.compile_bitmap(masks))
+        assert _validate_bm(1, 2, 2, N, B, bits) == cal.OK, cal.last_error()
+        assert _validate_bm(1, 2, 2, N, B, bits, t=0, l=1) == cal.OK
+        if nb % 64:
+            bad = bits.copy()
+            bad[3, -1] |= np.uint64(1) << np.uint64(63)      # a bit past nb
+            assert _validate_bm(1, 2, 2, N, B, bad) == INVALID and "past nb" in cal.last_error()
+            # the record holding row 3 is (0, 0); record (0, 1) is still fine
+            assert _validate_bm(1, 2, 2, N, B, bad, t=0, l=0) == INVALID
+            assert _validate_bm(1, 2, 2, N, B, bad, t=0, l=1) == cal.OK
+        assert _validate_bm(1, 2, 2, N, B, bits, words=-(-nb // 64) + 1) == INVALID
+
+
+def test_bitmap_calls_reject_bad_views():
+    view = cal.BitmapView(1, 1, 2, 1000, 128, 8, 2, P)     # words must be ceil(8/64) = 1
+    st = lib.calibatt_block_sparse_attn_bm(P, P, P, P, None, 2, 1000, 128, cal.BF16, 0.088, ctypes.byref(view), 0, 0,
+                                           None, 0, None)
+    assert st == INVALID and "words" in cal.last_error()
+    assert lib.calibatt_block_sparse_attn_bm(P, P, P, P, None, 2, 1000, 128, cal.BF16, 0.088, None, 0, 0, None, 0,
+                                             None) == INVALID
+    assert lib.calibatt_compile_bitmap(None, 1, 1, 1, 100, 10, P, None) == INVALID
+    assert lib.calibatt_compile_bitmap(P, 1, 1, 1, 100, 10, P + 4, None) == INVALID    # not 8-byte aligned
