@@ -441,8 +441,9 @@ def calibration_bench(args):
 
 def dictionary_run(args):
     """Wan-720p denoising-run dictionary (T=50, L=40, H=40): 27.9 GB of block masks generated on the GPU,
-    compiled into index lists and into runs in one call each; memory of each form; then every layer call
-    of the chosen timesteps (record (t, l) selected from the resident dictionary), through the runs."""
+    compiled into index lists, runs and bitmaps in one call each; memory of each form; then every layer
+    call of the chosen timesteps (record (t, l) selected from the resident dictionary), through the runs
+    and through the bitmaps."""
     import torch
     import workloads
     import calibrated_block_sparse_skiplist_amd as cal
@@ -473,6 +474,8 @@ def dictionary_run(args):
     sl = cal.compile_skiplist(masks, cfg.N, cfg.B)
     csr_ms = timed(lambda: cal.calibatt_compile_skiplist(masks, T, L, H, cfg.N, cfg.B, sl.row_ptr, sl.col_idx,
                                                          sl.col_idx.numel(), sl.order, stream))
+    bm = cal.compile_bitmap(masks, cfg.N, cfg.B)
+    bm_ms = timed(lambda: cal.calibatt_compile_bitmap(masks, T, L, H, cfg.N, cfg.B, bm.bits, stream))
     n_iv, nnz = il.n_iv, sl.nnz
     # block sizes for the work of each record
     sizes = torch.from_numpy(block_sizes(cfg.N, cfg.B)).to(dev, torch.float64)
@@ -488,6 +491,7 @@ def dictionary_run(args):
     anchors = W.equally_spaced_anchor_rows(cfg.R, cfg.n_anchor)
     scale = float(np.float32(1.0 / np.sqrt(cfg.d)))
     per_step = []
+    bm_bytes = bm.bits.numel() * 8
     for t in [int(x) for x in args.run_steps.split(",")]:
         cal.calibatt_layer_dispatch_iv(qd, kd, vd, o, None, il, t, 0, flags, cfg.F, cfg.R, cfg.C, anchors,
                                        scale=scale, stream=stream)
@@ -505,7 +509,16 @@ def dictionary_run(args):
             sp = torch.from_numpy(flags[t, l] == 0).to(dev)
             flop += float(4 * cfg.d * (tok[None] * masks[t, l][sp].to(torch.float64)).sum().item())
             flop += float((~sp).sum().item()) * anchor_head_flops(cfg.F, len(anchors), cfg.C, cfg.N, cfg.d)
+        # the same 40 layer calls through the bitmap form
+        a.record(stream)
+        for l in range(L):
+            cal.calibatt_layer_dispatch_bm(qd, kd, vd, o, None, bm, t, l, flags, cfg.F, cfg.R, cfg.C, anchors,
+                                           scale=scale, stream=stream)
+        b.record(stream)
+        torch.cuda.synchronize()
+        ms_bm = a.elapsed_time(b)
         per_step.append({"t": t, "layers": L, "ms_total": round(ms, 2), "ms_per_layer": round(ms / L, 3),
+                         "ms_per_layer_bitmap_form": round(ms_bm / L, 3),
                          "kept_fraction": round(float(masks[t].float().mean().item()), 4),
                          "tflops": round(flop / (ms * 1e-3) / 1e12, 1)})
     print(json.dumps({
@@ -513,8 +526,10 @@ def dictionary_run(args):
         "mask_generation_s": round(gen_s, 2), "records": T * L * H, "rows": rows, "nb": nb,
         "kept_blocks": kept, "kept_fraction": round(kept / mask_bytes, 4), "runs": n_iv,
         "bytes": {"masks": mask_bytes, "index_form": 8 * (rows + 1) + 4 * nnz + 4 * rows,
-                  "interval_form": 8 * (rows + 1) + 4 * n_iv + 4 * rows},
-        "compile_ms": {"index_form": round(csr_ms, 2), "interval_form": round(iv_ms, 2)},
+                  "interval_form": 8 * (rows + 1) + 4 * n_iv + 4 * rows,
+                  "interval_form_runs_only": 4 * n_iv, "bitmap_form": bm_bytes},
+        "compile_ms": {"index_form": round(csr_ms, 2), "interval_form": round(iv_ms, 2),
+                       "bitmap_form": round(bm_ms, 2)},
         "compile_GBps_masks_read_twice": round(2 * mask_bytes / (iv_ms * 1e-3) / 1e9, 1),
         "layer_calls": per_step}), flush=True)
 
@@ -847,6 +862,25 @@ def main():
                  "list_bytes_interval_form": 8 * (rows + 1) + 4 * il.n_iv}
     del il
 
+    # the same layer through the bitmap form (one bit per key block)
+    bm = cal.compile_bitmap(masks, cfg.N, cfg.B)
+    t_c = time.perf_counter()
+    for _ in range(5):
+        cal.calibatt_compile_bitmap(masks, T, L, H, cfg.N, cfg.B, bm.bits, stream)
+    torch.cuda.synchronize()
+    compile_bm_ms = (time.perf_counter() - t_c) * 1e3 / 5
+    cal.calibatt_layer_dispatch_bm(q, k, v, o, None, bm, 0, 0, wl.rep_flags, cfg.F, cfg.R, cfg.C, wl.anchors,
+                                   scale=wl.scale, stream=stream)
+    e0.record(stream)
+    for _ in range(reps):
+        cal.calibatt_layer_dispatch_bm(q, k, v, o, None, bm, 0, 0, wl.rep_flags, cfg.F, cfg.R, cfg.C, wl.anchors,
+                                       scale=wl.scale, stream=stream)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    bitmap = {"words_per_row": bm.bits.shape[1], "compile_ms": round(compile_bm_ms, 3),
+              "layer_call_ms": round(e0.elapsed_time(e1) / reps, 3), "bytes": bm.bits.numel() * 8}
+    del bm
+
     dense_ms = None
     if not args.no_dense:
         ones = torch.ones((1, 1, H, nb, nb), dtype=torch.uint8, device=dev)
@@ -914,6 +948,7 @@ def main():
         "layer_call_with_lse_ms": round(layer_lse_ms, 3),
         "layer_call_protocol": protocol,
         "intervals": intervals,
+        "bitmap": bitmap,
         "sparsity": {"token_sparse_heads": work["token_sparsity_sparse_heads"],
                      "block_sparse_heads": work["block_sparsity_sparse_heads"],
                      "anchor_query": work["anchor_query_sparsity"],
