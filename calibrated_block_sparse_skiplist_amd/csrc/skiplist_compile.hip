@@ -413,24 +413,50 @@ hipError_t scan_counts(int64_t rows, int64_t* row_ptr, hipStream_t s) {
 }
 
 // Bitmap form: row r's key block c is bit c % 64 of word c / 64 of the row's
-// `words` words. One wave per row (waves stride over rows): word w is the
-// ballot of "byte 64w + lane of the row is nonzero" over the wave's lanes, so
-// one coalesced 64-byte load gives one word; lane w keeps word w and the
-// row's words are stored together. Columns past nb read nothing and stay 0.
+// `words` words. One wave per row, waves striding over rows two at a time. A
+// window is 60 of the row's aligned 16-byte chunks (each lane loads one chunk
+// of 64; the last 4 are the next window's first) and yields 15 words. With off
+// = the row's first byte's place in its first chunk, the window's word k is
+// bits 64k + off .. 64k + off + 63 of its chunk-bit stream: chunks 4k .. 4k + 4.
+// Bytes outside the row count as 0, so the padding bits past nb stay 0.
+constexpr int kWinChunks = 60;
+constexpr int kWinWords = kWinChunks / 4;
+
+__device__ __forceinline__ uint64_t window_word(uint32_t x, int lane, int off) {
+  const int src = (4 * lane) & 63;   // lanes >= kWinWords compute a word that is not stored
+  const uint64_t a0 = (uint32_t)__shfl((int)x, src);
+  const uint64_t a1 = (uint32_t)__shfl((int)x, src + 1);
+  const uint64_t a2 = (uint32_t)__shfl((int)x, src + 2);
+  const uint64_t a3 = (uint32_t)__shfl((int)x, src + 3);
+  const uint64_t a4 = (uint32_t)__shfl((int)x, (src + 4) & 63);
+  uint64_t w = (a0 >> off) | (a1 << (16 - off)) | (a2 << (32 - off)) | (a3 << (48 - off));
+  if (off) w |= a4 << (64 - off);
+  return w;
+}
+
 __global__ __launch_bounds__(kThreads) void bitmap_kernel(const uint8_t* __restrict__ masks, int64_t rows, int nb,
                                                           int words, uint64_t* __restrict__ bits) {
   const int lane = threadIdx.x & 63;
+  const int mis = (int)((uintptr_t)masks & 15);
+  const int64_t total = rows * nb;
   const int64_t stride = (int64_t)gridDim.x * kWaves;
-  for (int64_t r = (int64_t)blockIdx.x * kWaves + (threadIdx.x >> 6); r < rows; r += stride) {
-    const uint8_t* row = masks + r * nb;
-    uint64_t mine = 0;
-    for (int w = 0; w < words; ++w) {
-      const int c = 64 * w + lane;
-      const bool keep = c < nb && row[c] != 0;
-      const uint64_t word = __ballot(keep);
-      if (lane == w) mine = word;
+  for (int64_t ra = (int64_t)blockIdx.x * kWaves + (threadIdx.x >> 6); ra < rows; ra += 2 * stride) {
+    const int64_t rb = ra + stride;
+    const bool has_b = rb < rows;
+    const RowSpan a = row_span(ra, nb, mis);
+    const RowSpan b = row_span(has_b ? rb : ra, nb, mis);
+    for (int w0 = 0; w0 < words; w0 += kWinWords) {
+      const int64_t c0 = (int64_t)w0 / kWinWords * kWinChunks * 16 + 16 * lane;
+      const uint32_t xa = chunk_bits(masks, total, a.s, a.e, a.cs0 + c0);
+      const uint32_t xb = chunk_bits(masks, total, b.s, b.e, b.cs0 + c0);
+      const uint64_t wa = window_word(xa, lane, (int)(a.s - a.cs0));
+      const uint64_t wb = window_word(xb, lane, (int)(b.s - b.cs0));
+      const int k = w0 + lane;
+      if (lane < kWinWords && k < words) {
+        bits[ra * words + k] = wa;
+        if (has_b) bits[rb * words + k] = wb;
+      }
     }
-    if (lane < words) bits[r * words + lane] = mine;
   }
 }
 

@@ -34,6 +34,23 @@ def test_compile_matches_oracle(shape, p, seed):
     cal.calibatt_validate_bitmap(bm)
 
 
+@pytest.mark.parametrize("nb,shift", [(591, 1), (591, 7), (1030, 15), (64, 9), (5, 3)])
+def test_compile_unaligned_masks(nb, shift):
+    """Masks that start off a 16-byte boundary (a view into a larger buffer): the kernel's chunk alignment
+    moves with the base address."""
+    rng = np.random.default_rng(nb + shift)
+    T, L, H = 1, 2, 3
+    masks = (rng.random((T, L, H, nb, nb)) < 0.4).astype(np.uint8)
+    buf = torch.full((masks.size + 32,), 255, dtype=torch.uint8, device="cuda")
+    view = buf[shift:shift + masks.size].view(T, L, H, nb, nb)
+    view.copy_(torch.from_numpy(masks).cuda())
+    assert view.data_ptr() % 16 == shift % 16
+    say(f"[bitmap] compile unaligned nb={nb} shift={shift}")
+    bm = cal.compile_bitmap(view, nb * 8, 8)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(_bits_np(bm), oracle.compile_bitmap(masks))
+
+
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 @pytest.mark.parametrize("N,d,B", [(1000, 128, 128), (700, 64, 64), (1500, 64, 128), (300, 128, 64)])
 @pytest.mark.parametrize("with_lse", [True, False])
