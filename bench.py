@@ -668,6 +668,9 @@ def profile_workload(kind: str):
         for _ in range(3):
             cal.calibatt_compile_skiplist(masks, 1, 1, cfg.H, cfg.N, cfg.B, sl.row_ptr, sl.col_idx,
                                           sl.col_idx.numel(), None)
+        bm = cal.compile_bitmap(masks, cfg.N, cfg.B)
+        for _ in range(3):
+            cal.calibatt_compile_bitmap(masks, 1, 1, cfg.H, cfg.N, cfg.B, bm.bits)
         for _ in range(3):
             cal.calibatt_layer_dispatch(q, k, v, o, None, sl, 0, 0, wl.rep_flags, cfg.F, cfg.R, cfg.C, wl.anchors,
                                         scale=wl.scale)
