@@ -32,7 +32,11 @@
  *    path, fp32 accumulation and softmax) or fp32 (a correctness path with
  *    fp32 arithmetic throughout). scale must be finite and > 0.
  *  - `stream` is a hipStream_t passed as void* (NULL = the null stream). The
- *    attention calls are asynchronous: they only enqueue kernels on `stream`.
+ *    attention calls are asynchronous: they only enqueue kernels on `stream`
+ *    (no allocation, memset or host synchronisation), so they can be captured
+ *    into a HIP graph and replayed; so can calibatt_compile_bitmap. The index
+ *    and run compiles read a count back (a host sync) and checked mode reads
+ *    the lists back: neither can be captured.
  *  - Errors: arguments are checked on the host before anything is enqueued.
  *    A bad argument returns CALIBATT_ERR_INVALID_ARG and touches no output; a
  *    failed HIP call returns CALIBATT_ERR_HIP. calibatt_last_error() then
