@@ -113,6 +113,8 @@ calibatt_status_t view_of(const calibatt_intervals_t* il, ListView* v) {
 calibatt_status_t view_of(const calibatt_bitmap_t* bm, ListView* v) {
   if (!bm) return fail(CALIBATT_ERR_INVALID_ARG, "bitmap view is NULL");
   if (!bm->bits) return fail(CALIBATT_ERR_INVALID_ARG, "bitmap bits are NULL");
+  if (reinterpret_cast<uintptr_t>(bm->bits) % 8 != 0)
+    return fail(CALIBATT_ERR_INVALID_ARG, "bitmap bits are not 8-byte aligned");
   if (bm->nb < 1 || bm->words != ceil_div(bm->nb, 64))
     return fail(CALIBATT_ERR_INVALID_ARG, "bitmap words (%d) != ceil(nb/64) with nb = %d", bm->words, bm->nb);
   *v = {bm->T, bm->L, bm->H, bm->N, bm->B, bm->nb, nullptr, nullptr, nullptr, nullptr, bm->bits, bm->words};

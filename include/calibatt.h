@@ -243,7 +243,8 @@ calibatt_status_t calibatt_layer_dispatch_iv(const void* q, const void* k, const
  * caller-owned device memory, as produced by calibatt_compile_bitmap.
  *   T, L, H, N, B, nb: as in calibatt_skiplist_t.
  *   words : ceil(nb / 64).
- *   bits  : uint64 [T*L*H*nb][words].
+ *   bits  : uint64 [T*L*H*nb][words], device, 8-byte aligned (a view that is
+ *           not is rejected with CALIBATT_ERR_INVALID_ARG).
  */
 typedef struct {
   int32_t T, L, H, N, B, nb, words;

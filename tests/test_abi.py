@@ -410,3 +410,7 @@ def test_bitmap_calls_reject_bad_views():
                                              None) == INVALID
     assert lib.calibatt_compile_bitmap(None, 1, 1, 1, 100, 10, P, None) == INVALID
     assert lib.calibatt_compile_bitmap(P, 1, 1, 1, 100, 10, P + 4, None) == INVALID    # not 8-byte aligned
+    view = cal.BitmapView(1, 1, 2, 1000, 128, 8, 1, P + 4)  # the kernels read whole 64-bit words
+    st = lib.calibatt_block_sparse_attn_bm(P, P, P, P, None, 2, 1000, 128, cal.BF16, 0.088, ctypes.byref(view), 0, 0,
+                                           None, 0, None)
+    assert st == INVALID and "aligned" in cal.last_error()
