@@ -258,8 +258,11 @@ void attn_bf16_kernel(const AttnParams p) {
 
   // Key blocks in visiting order (uniform across the workgroup). Index lists
   // and anchor items are indexed by step; runs are walked with a cursor
-  // (current run, its end), advanced once per block.
+  // (current run, its end), advanced once per block. The LDS entry a block
+  // change needs (the next index, or the next run) is read one stage before
+  // the change (pf_next), so its latency is not paid at a stage's start.
   int run_i = 0, run_hi = 0;
+  uint32_t pf_next = 0;
   auto first_block = [&]() -> int {
     if (it.runs) {
       const uint32_t w = __builtin_amdgcn_readfirstlane(lds_list32[0]);
@@ -271,11 +274,21 @@ void attn_bf16_kernel(const AttnParams p) {
   auto next_block = [&](int c, int i) -> int {   // i: step of the block that follows c
     if (it.runs) {
       if (c + 1 < run_hi) return c + 1;
-      const uint32_t w = __builtin_amdgcn_readfirstlane(lds_list32[++run_i]);
+      const uint32_t w = __builtin_amdgcn_readfirstlane(pf_next);   // lds_list32[run_i + 1]
+      ++run_i;
       run_hi = (int)(w >> 16);
       return (int)(w & 0xffffu);
     }
-    return idx_list ? __builtin_amdgcn_readfirstlane((int)lds_list[i]) : i;
+    // lds_list[i]: the 16-bit half of the word read at step i's first stage
+    return idx_list ? (int)((__builtin_amdgcn_readfirstlane(pf_next) >> (16 * (i & 1))) & 0xffffu) : i;
+  };
+  // At the first stage of a block, the 32-bit LDS word next_block will need at
+  // its last: the next run, or the word holding the next index (one load, its
+  // address a uniform select; the list area holds kListCap/2 words, so every
+  // word index below stays in it).
+  auto prefetch_next = [&](int i) {   // i: step of the next block
+    const int word = it.runs ? min(run_i + 1, kListCap / 2 - 1) : min(i >> 1, kListCap / 2 - 1);
+    pf_next = lds_list32[word];
   };
 
   f32x16 oacc[DT];
@@ -370,6 +383,7 @@ void attn_bf16_kernel(const AttnParams p) {
     // ---- K_j and V_{j-1} resident in every wave's view; the other buffers are free ----
     wait_vmcnt<0>();
     barrier_no_fence();
+    if (half == 0) prefetch_next(j / SPB + 1);
     const StageSrc ksrc = stage_src(Kb, c_next, (j + 1) % SPB);
     const StageSrc vsrc = stage_src(Vb, c, half);
     // Copy step d of this stage: K_{j+1} first (when there is a next stage), then V_j.
