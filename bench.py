@@ -36,8 +36,9 @@ PEAK_BF16_TFLOPS = 2516.6     # MI355X dense bf16 MFMA: 256 CU x 2.4 GHz x 4096 
 PEAK_HBM_GBS = 8000.0
 ATTN_KERNEL = "attn_bf16_kernel"
 # Sources the bf16 attention kernel is compiled from (its own file and the headers it includes).
+# the kernel and its launch (api.hip fixes the grid's mapping to XCDs, which moves the counters too)
 ATTN_SOURCES = [os.path.join(ROOT, "calibrated_block_sparse_skiplist_amd", "csrc", f)
-                for f in ("attn_bf16.hip", "gfx950_device.h", "internal.h")]
+                for f in ("attn_bf16.hip", "gfx950_device.h", "internal.h", "api.hip")]
 
 
 def attn_source_sha() -> str:
