@@ -350,14 +350,17 @@ void fill_common(calibatt::AttnParams& p, const void* q, const void* k, const vo
   p.scale = scale;
   p.scale_log2 = scale * 1.4426950408889634f;
   // Work order: query blocks in block order (neighbours share key blocks), in
-  // runs of 64 consecutive items per XCD (as many as an XCD runs at once, two
-  // workgroups on each of its 32 CUs); heaviest-first order per record (the
-  // compiled `order`) measured no faster on the Wan-shaped layers, so the
-  // kernels do not read it. Each XCD's share of the grid is fixed by the
-  // round-robin dispatch, so when runs cover whole heads (nb divides or is a
-  // multiple of 8*64) the chunks turn per run: otherwise an XCD would take the
-  // same, lighter or heavier, slice of every head.
-  p.xcd_group = 64;
+  // runs of consecutive items per XCD: about as many as an XCD runs at once, so
+  // that the items running together start and walk their lists together (64 at
+  // d = 128, B = 128: two workgroups on each of an XCD's 32 CUs; the smaller
+  // variants run more at once; each value the fastest measured at the Wan-720p
+  // shape). Heaviest-first order per record (the compiled `order`) measured no
+  // faster on the Wan-shaped layers, so the kernels do not read it. Each XCD's
+  // share of the grid is fixed by the round-robin dispatch, so when runs cover
+  // whole heads (nb divides or is a multiple of 8 * xcd_group) the chunks turn
+  // per run: otherwise an XCD would take the same, lighter or heavier, slice of
+  // every head.
+  p.xcd_group = (d == 128 && blk == 128) ? 64 : (d == 64 && blk == 64) ? 192 : 128;
   p.xcd_rotate = p.nb > 0 && (p.nb % (8 * p.xcd_group) == 0 || (8 * p.xcd_group) % p.nb == 0) ? 1 : 0;
 }
 
